@@ -1,0 +1,251 @@
+#!/usr/bin/env python3
+"""Benchmark of libwallattn on one MI355X: Wall Attention prefill TFLOP/s at
+T = 8K and single-step decode GB/s over a 32K-token cache.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+
+One "step" is one call of wall_attn_fwd (running-sum pre-pass + attention)
+on the long-context workload B=1, T=8192, HQ=16, H=4, K=V=128, bf16, with
+g = -0.05*softplus(N(0,1)), g_scalar and sink_bias (inputs resident in HBM
+before timing starts).  ``value`` is its throughput in algorithmic TFLOP/s:
+2*HQ*(K+V) per visible (query, key) pair, only causal pairs counted.
+
+Also reported on the same JSON line:
+  roofline      the attention kernel alone (wall_attn_fwd_attend), timed with
+                HIP events on the launch stream, against the MI355X dense
+                fp16/bf16 MFMA peak;
+  decode        wall_attn_decode on B=64, T_kv=32768, HQ=32, H=8, K=V=128,
+                C=64: algorithmic bytes (k_tilde, v, r_cache, q, p_curr, o,
+                sink) per call over its event-timed duration, against HBM
+                peak; the cache build is reported beside it;
+  cpu_baseline  the fp64 CPU oracle timed on this host's cores over a row
+                sample of the prefill workload, scaled to TFLOP/s.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+METRIC = "prefill TFLOP/s (% bf16 MFMA peak) at T=8K; decode GB/s (% HBM peak)"
+PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-row-stride", type=int, default=16,
+                    help="oracle baseline evaluates every n-th query row")
+    return ap.parse_args()
+
+
+def causal_pairs(lengths, window=0):
+    tot = 0
+    for L in lengths:
+        if window <= 0 or window >= L:
+            tot += L * (L + 1) // 2
+        else:
+            tot += window * (window + 1) // 2 + (L - window) * window
+    return tot
+
+
+def event_time_ms(fn, n, torch):
+    """Average milliseconds of fn() over n back-to-back launches on the current stream."""
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(n):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def log(msg):
+    sys.stderr.write(msg + "\n")
+    sys.stderr.flush()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_attention_channel_amd as wa
+    from exact_attention_channel_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    lib = wa.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    # ------------------------------------------------------------------ prefill
+    c = W.PREFILL_T8192_BF16
+    log(f"[bench] prefill workload {c.name}: generating inputs")
+    x = W.make_prefill(c, device=dev)
+    B, T, HQ, H, K, V = c.B, c.T, c.HQ, c.H, c.K, c.V
+    o = torch.empty(B, T, HQ, V, dtype=c.dtype, device=dev)
+    lse = torch.empty(B, T, HQ, dtype=torch.float32, device=dev)
+    wsb = lib.wall_attn_fwd_workspace_bytes(B, T, HQ, H, K, V, 0, 0, wa.WA_BF16)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    scale = float(x["scale"])
+
+    def fwd():
+        rc = lib.wall_attn_fwd(ptr(x["q"]), ptr(x["k"]), ptr(x["v"]), ptr(x["g"]),
+                               ptr(x["g_scalar"]), ptr(x["sink_bias"]), ptr(o), ptr(lse),
+                               B, T, HQ, H, K, V, None, 0, 0, 0, scale, wa.WA_BF16,
+                               ptr(ws), wsb, stream)
+        if rc:
+            raise RuntimeError(lib.wall_attn_last_error().decode())
+
+    def prepare():
+        rc = lib.wall_attn_fwd_prepare(ptr(x["q"]), ptr(x["k"]), ptr(x["g"]), ptr(x["g_scalar"]),
+                                       B, T, HQ, H, K, V, None, 0, 0, scale, wa.WA_BF16,
+                                       ptr(ws), wsb, stream)
+        if rc:
+            raise RuntimeError(lib.wall_attn_last_error().decode())
+
+    def attend():
+        rc = lib.wall_attn_fwd_attend(ptr(x["v"]), ptr(x["g_scalar"]), ptr(x["sink_bias"]),
+                                      ptr(o), ptr(lse), B, T, HQ, H, K, V, None, 0, 0, 0,
+                                      wa.WA_BF16, ptr(ws), wsb, stream)
+        if rc:
+            raise RuntimeError(lib.wall_attn_last_error().decode())
+
+    flops = 2.0 * HQ * (K + V) * causal_pairs([T] * B)
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` full forward passes between events
+    ms_step = event_time_ms(fwd, args.steps, torch)
+    log(f"[bench] prefill step {ms_step:.4f} ms")
+    ms_prep = event_time_ms(prepare, args.steps, torch)
+    ms_attn = event_time_ms(attend, args.steps, torch)
+    log(f"[bench] prepare {ms_prep:.4f} ms, attend {ms_attn:.4f} ms")
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    attn_tflops = flops / (ms_attn * 1e-3) / 1e12
+    del ws, o, lse, x
+    torch.cuda.empty_cache()
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c.name, "B": B, "T": T, "HQ": HQ, "H": H, "K": K, "V": V,
+                   "causal": True, "g": "-0.05*softplus(N(0,1))", "g_scalar": True,
+                   "sink_bias": True, "gflop_per_step": round(flops / 1e9, 3)},
+        "roofline": {"kernel": "k_attn_fwd_bf16 (wall_attn_fwd_attend)", "bound": "mfma",
+                     "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
+                     "traffic": None, "kernel_ms": round(ms_attn, 4)},
+        "prefill_breakdown_ms": {"prepare": round(ms_prep, 4), "attend": round(ms_attn, 4)},
+    }
+
+    # ------------------------------------------------------------------ decode
+    if not args.no_decode:
+        d = W.DECODE_T32768_BF16
+        log(f"[bench] decode workload {d.name}: generating inputs on the GPU")
+        y = W.make_decode(d, device=dev)
+        P = wa.wall_attn_prefix_log2(y["g"])
+        del y["g"]
+        torch.cuda.empty_cache()
+        kt, rc_ = wa.build_wall_kv_cache(y["k"], P, chunk_size=d.C)
+        pc = P[:, -1:].contiguous()
+        def build():
+            r = lib.wall_attn_build_kv_cache(ptr(y["k"]), ptr(P), ptr(kt), ptr(rc_), d.B, d.T_kv,
+                                             d.HQ, d.H, d.K, d.C, wa.WA_BF16, stream)
+            if r:
+                raise RuntimeError(lib.wall_attn_last_error().decode())
+
+        build_ms = event_time_ms(build, 3, torch)
+        del P
+        torch.cuda.empty_cache()
+        do = torch.empty(d.B, 1, d.HQ, d.V, dtype=d.dtype, device=dev)
+        dl = torch.empty(d.B, 1, d.HQ, dtype=torch.float32, device=dev)
+        dwb = lib.wall_attn_decode_workspace_bytes(d.B, d.T_kv, d.HQ, d.H, d.K, d.V, d.C)
+        dws = torch.empty(dwb, dtype=torch.uint8, device=dev)
+        dscale = float(y["scale"])
+
+        def dec():
+            r = lib.wall_attn_decode(ptr(y["q"]), ptr(y["v"]), ptr(pc), ptr(kt), ptr(rc_),
+                                     ptr(y["sink_bias"]), ptr(do), ptr(dl), d.B, d.T_kv, d.HQ,
+                                     d.H, d.K, d.V, d.C, dscale, wa.WA_BF16, ptr(dws), dwb,
+                                     stream)
+            if r:
+                raise RuntimeError(lib.wall_attn_last_error().decode())
+
+        for _ in range(args.warmup):
+            dec()
+        dms = event_time_ms(dec, args.steps, torch)
+        nc = -(-d.T_kv // d.C)
+        dbytes = (kt.numel() * kt.element_size() + y["v"].numel() * 2 + rc_.numel() * 4
+                  + y["q"].numel() * 2 + pc.numel() * 4 + do.numel() * 2
+                  + (0 if y["sink_bias"] is None else d.HQ * 4))
+        assert rc_.shape[1] == nc
+        gbs = dbytes / (dms * 1e-3) / 1e9
+        log(f"[bench] decode {dms:.4f} ms, {gbs:.1f} GB/s; cache build {build_ms:.3f} ms")
+        k_bytes = y["k"].numel() * 2
+        build_bytes = (k_bytes + d.B * d.T_kv * d.HQ * d.K * 4 + kt.numel() * kt.element_size()
+                       + rc_.numel() * 4)
+        out["decode"] = {
+            "workload": d.name, "metric": "decode GB/s", "value": round(gbs, 1), "unit": "GB/s",
+            "ms_per_call": round(dms, 4), "bytes_per_call": dbytes,
+            "roofline": {"kernel": "k_decode_split + k_decode_combine (wall_attn_decode)",
+                         "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+            "cache_build": {"ms": round(build_ms, 3),
+                            "GB/s": round(build_bytes / (build_ms * 1e-3) / 1e9, 1)},
+        }
+        del kt, rc_, y, dws, do, dl, pc
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        import oracle
+        cx = W.make_prefill(c)
+        stride = max(1, args.cpu_row_stride)
+        rows = list(range(stride - 1, T, stride))
+        sample_flops = 2.0 * HQ * (K + V) * sum(r + 1 for r in rows)
+        log(f"[bench] cpu baseline: oracle over {len(rows)} rows on {oracle.num_threads()} threads")
+        t0 = time.perf_counter()
+        oracle.wall_attn(cx["q"], cx["k"], cx["v"], cx["g"], scale=cx["scale"],
+                         g_scalar=cx["g_scalar"], sink_bias=cx["sink_bias"], rows=rows)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {
+            "value": round(sample_flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"every {stride}th query row of {c.name} ({len(rows)} rows x {HQ} heads, "
+                      f"{sample_flops / 1e9:.1f} GFLOP algorithmic) in {dt:.2f} s; "
+                      "TFLOP/s = sample FLOPs / wall time",
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

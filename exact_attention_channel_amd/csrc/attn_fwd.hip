@@ -1,0 +1,454 @@
+// Prefill attention with the Wall Attention per-channel decay (gfx950).
+//
+// Wall Attention README, introduction: the score of query i and key j weights
+// channel n of q_i . k_j by exp(P[i,n] - P[j,n]), P the running sum of the
+// learned decay g; "Usage" adds GQA, the scalar gate g_scalar, sink_bias,
+// window_size and cu_seqlens.  The pre-pass (prefix.hip) has already written
+//   q_hat_i   = q_i * 2^(P2_i - RQ_I) * scale * log2(e)     (query tile anchor RQ_I)
+//   k_tilde_j = k_j * 2^(R_J - P2_j)                        (key chunk anchor R_J)
+// so for a query tile I and a 64-key tile J the decayed scores are one dense
+// product: S = q_hat . (k_tilde * d_IJ)^T with d_IJ[n] = 2^(RQ_I[n] - R_J[n]),
+// K exponentials per tile pair instead of K per (i, j) pair.  Scores are in
+// log2 units, so the online softmax (FlashAttention's running max and sum,
+// see the FlashAttention papers' tiling with rescaled partial outputs) uses
+// exp2 directly.
+//
+// bf16 inputs: the rescaled q/k operands are IEEE half (3 more mantissa bits
+// than bfloat16, which keeps the rounding of large decayed scores within
+// tolerance); P and V stay bfloat16.  If a key tile's inter-tile factor
+// d_IJ exceeds 2^8 (the decay sum grew between the key tile and the query
+// tile) the tile is staged as d_IJ * 2^-sigma with an integer sigma and the
+// scores are multiplied back by 2^sigma, so the half operands cannot
+// overflow; a channel pushed below the half range that way is smaller than
+// the dominant one by more than 2^20 and does not change the score.
+//
+// Kernel layout: 256 threads = 4 waves x 32 query rows; per tile the workgroup
+// stages the decayed key tile (row-major) and the value tile (transposed) in
+// LDS.  Each wave computes S^T = K_hat Q_hat^T with v_mfma_f32_32x32x16_f16
+// so that a lane holds one query column: the row max and sum are in-lane
+// plus one swap between the two half-waves, and the probabilities feed the
+// next MFMA (O^T += V^T P^T, bf16) as its B operand without leaving registers.
+// Tiles outside the causal / window / sequence range are never visited and
+// only boundary tiles are masked element by element (the block-sparse idea
+// of FlexAttention's BlockMask, computed from indices instead of stored).
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace wa {
+namespace {
+
+constexpr int BN = CHUNK;  // keys per tile
+constexpr int WROWS = 32;  // query rows per wave
+
+template <int DK, int DV, bool HAS_GS>
+__global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
+    const _Float16 *__restrict__ qh, const _Float16 *__restrict__ kt, const bf16_t *__restrict__ v,
+    const float *__restrict__ anch, const float *__restrict__ gsum,
+    const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
+    const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int nseg, int NCmax, int NQT,
+    int64_t window) {
+  constexpr int KS = DK + 8;  // LDS row stride (elements) of the key tile
+  constexpr int VS = BN + 8;  // LDS row stride (elements) of the transposed value tile
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];  // half bits
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[DV * VS];
+  __shared__ float Gj[BN];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hq = blockIdx.x % HQ;
+  const int rest = blockIdx.x / HQ;
+  const int seg = rest % nseg;
+  const int I = NQT - 1 - rest / nseg;  // longest query tiles first
+  int64_t bos, eos;
+  segment_bounds(seg, T, cu, bos, eos);
+  const int64_t L = eos - bos;
+  const int nqt = (int)((L + QTILE - 1) / QTILE);
+  if (I >= nqt) return;
+  const int h = hq / (HQ / H);
+  const int64_t i0 = bos + (int64_t)I * QTILE;
+  const int64_t i_last = min(i0 + QTILE, eos) - 1;
+  const int64_t jlo_blk = window > 0 ? max(bos, i0 - window + 1) : bos;
+  const int Jlo = (int)((jlo_blk - bos) / BN), Jhi = (int)((i_last - bos) / BN);
+
+  const int64_t qw0 = i0 + wave * WROWS;
+  const bool wave_live = qw0 < eos;
+  const int64_t qw_last = min(qw0 + WROWS, eos) - 1;
+  const int64_t jw_lo = window > 0 ? max(bos, qw0 - window + 1) : bos;
+
+  const int col = lane & 31, half = lane >> 5;
+  const int64_t qi = qw0 + col;
+  const bool q_ok = qi < eos;
+
+  f16x8 qB[DK / 16];
+#pragma unroll
+  for (int ks = 0; ks < DK / 16; ++ks) {
+    if (q_ok)
+      qB[ks] = *reinterpret_cast<const f16x8 *>(qh + (qi * HQ + hq) * DK + ks * 16 + half * 8);
+    else
+      qB[ks] = f16x8{};
+  }
+  const float g_i = (HAS_GS && q_ok) ? gsum[qi * HQ + hq] : 0.f;
+
+  // staging roles
+  constexpr int KCP = DK / 8;      // 16-byte pieces per key row
+  constexpr int KRP = 256 / KCP;   // key rows per pass
+  constexpr int KNP = BN / KRP;    // passes
+  const int cp = tid % KCP, kr = tid / KCP;
+  constexpr int VNB = (DV / 8) * 16;  // 4-key x 8-channel blocks of the value tile
+  const int kq = tid % 16, cg = tid / 16;
+  const bool v_role = tid < VNB;
+  const int sq = kq & 3;
+  const int vpos = 16 * (kq >> 2) + 4 * (sq >> 1) + 8 * (sq & 1);
+
+  const int64_t cbase = (int64_t)seg * NCmax;
+  const int cq = 2 * I;  // the query tile's anchor: its first chunk
+  float RQ[8];
+  {
+    const float *ap = anch + ((cbase + cq) * HQ + hq) * DK + cp * 8;
+    const float4 a0 = *reinterpret_cast<const float4 *>(ap);
+    const float4 a1 = *reinterpret_cast<const float4 *>(ap + 4);
+    RQ[0] = a0.x; RQ[1] = a0.y; RQ[2] = a0.z; RQ[3] = a0.w;
+    RQ[4] = a1.x; RQ[5] = a1.y; RQ[6] = a1.z; RQ[7] = a1.w;
+  }
+
+  u32x4 kreg[KNP];
+  u32x4 vreg[4];
+  float dreg[8];
+  float gj_reg = 0.f;
+  float csig_next = 1.f;  // 2^sigma of the tile being loaded
+
+  auto load_tile = [&](int J) {
+    const int64_t kj0 = bos + (int64_t)J * BN;
+    const float *ap = anch + ((cbase + J) * HQ + hq) * DK + cp * 8;
+    const float4 a0 = *reinterpret_cast<const float4 *>(ap);
+    const float4 a1 = *reinterpret_cast<const float4 *>(ap + 4);
+    dreg[0] = RQ[0] - a0.x; dreg[1] = RQ[1] - a0.y; dreg[2] = RQ[2] - a0.z; dreg[3] = RQ[3] - a0.w;
+    dreg[4] = RQ[4] - a1.x; dreg[5] = RQ[5] - a1.y; dreg[6] = RQ[6] - a1.z; dreg[7] = RQ[7] - a1.w;
+    // largest log2 factor over all channels: every group of KCP consecutive
+    // lanes holds all channel pieces
+    float emax = dreg[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) emax = fmaxf(emax, dreg[e]);
+#pragma unroll
+    for (int o = 1; o < KCP; o <<= 1) emax = fmaxf(emax, __shfl_xor(emax, o));
+    const float sigma = emax > 8.f ? ceilf(emax - 8.f) : 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dreg[e] -= sigma;
+    csig_next = fast_exp2(sigma);
+#pragma unroll
+    for (int p = 0; p < KNP; ++p) {
+      const int64_t row = kj0 + kr + p * KRP;
+      kreg[p] = row < eos ? *reinterpret_cast<const u32x4 *>(kt + (row * HQ + hq) * DK + cp * 8)
+                          : u32x4{0, 0, 0, 0};
+    }
+    if (v_role) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = kj0 + 4 * kq + r;
+        vreg[r] = row < eos ? *reinterpret_cast<const u32x4 *>(v + (row * H + h) * DV + cg * 8)
+                            : u32x4{0, 0, 0, 0};
+      }
+    }
+    if (HAS_GS && tid < BN) {
+      const int64_t row = kj0 + tid;
+      gj_reg = row < eos ? gsum[row * HQ + hq] : 0.f;
+    }
+  };
+
+  auto store_tile = [&]() {
+    float d[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) d[e] = fast_exp2(dreg[e]);
+#pragma unroll
+    for (int p = 0; p < KNP; ++p) {
+      u32x4 w = kreg[p], out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[e] = pack_f16x2(f16_lo(w[e]) * d[2 * e], f16_hi(w[e]) * d[2 * e + 1]);
+      *reinterpret_cast<u32x4 *>(&Ks[(kr + p * KRP) * KS + cp * 8]) = out;
+    }
+    if (v_role) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int wi = c >> 1;
+        u32x2 out;
+        if (c & 1) {
+          out.x = (vreg[0][wi] >> 16) | (vreg[1][wi] & 0xffff0000u);
+          out.y = (vreg[2][wi] >> 16) | (vreg[3][wi] & 0xffff0000u);
+        } else {
+          out.x = (vreg[0][wi] & 0xffffu) | (vreg[1][wi] << 16);
+          out.y = (vreg[2][wi] & 0xffffu) | (vreg[3][wi] << 16);
+        }
+        *reinterpret_cast<u32x2 *>(&Vt[(cg * 8 + c) * VS + vpos]) = out;
+      }
+    }
+    if (HAS_GS && tid < BN) Gj[tid] = gj_reg;
+  };
+
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 oacc[DV / 32];
+#pragma unroll
+  for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = f32x16{};
+
+  load_tile(Jlo);
+  store_tile();
+  float csig = csig_next;  // 2^sigma of the tile in LDS
+  for (int J = Jlo; J <= Jhi; ++J) {
+    __syncthreads();
+    if (J < Jhi) load_tile(J + 1);
+    const int64_t kj0 = bos + (int64_t)J * BN;
+    const bool need = wave_live && kj0 <= qw_last && kj0 + BN - 1 >= jw_lo;
+    if (need) {
+      f32x16 S[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        S[sb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < DK / 16; ++ks) {
+          const f16x8 a =
+              *reinterpret_cast<const f16x8 *>(&Ks[(sb * 32 + col) * KS + ks * 16 + half * 8]);
+          S[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[ks], S[sb], 0, 0, 0);
+        }
+      }
+      const bool masked =
+          (kj0 + BN - 1 > qw0) || (window > 0 && qw0 + WROWS - 1 - kj0 >= window);
+      float cs = csig;  // scores are S * cs until folded in below
+      if (HAS_GS || masked) {
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            float s = S[sb][r] * cs;
+            if (HAS_GS) s += g_i - Gj[kk];
+            if (masked) {
+              const int64_t j = kj0 + kk;
+              if (j > qi || (window > 0 && qi - j >= window)) s = -INFINITY;
+            }
+            S[sb][r] = s;
+          }
+        }
+        cs = 1.f;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * cs;
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(S[sb][r], cs, -m_use));
+          S[sb][r] = p;
+          rs += p;
+        }
+      rs += __shfl_xor(rs, 32);
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] *= alpha;
+      bf16x8 pB[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)S[s >> 1][8 * (s & 1) + e];
+#pragma unroll
+      for (int mb = 0; mb < DV / 32; ++mb) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8 *>(&Vt[(mb * 32 + col) * VS + s * 16 + half * 8]);
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[s], oacc[mb], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+    if (J < Jhi) store_tile();
+    csig = csig_next;
+  }
+
+  if (!q_ok) return;
+  float mf = m_run, Z = l_run;
+  if (sink != nullptr) {
+    const float s2 = sink[hq] * LOG2E;
+    mf = fmaxf(m_run, s2);
+    Z = l_run * fast_exp2(m_run - mf) + fast_exp2(s2 - mf);
+  }
+  const float inv = fast_exp2(m_run - mf) / Z;
+  bf16_t *orow = o + (qi * HQ + hq) * DV;
+#pragma unroll
+  for (int mb = 0; mb < DV / 32; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      u32x2 w;
+      w.x = pack_bf16x2(oacc[mb][4 * j] * inv, oacc[mb][4 * j + 1] * inv);
+      w.y = pack_bf16x2(oacc[mb][4 * j + 2] * inv, oacc[mb][4 * j + 3] * inv);
+      *reinterpret_cast<u32x2 *>(orow + mb * 32 + 8 * j + 4 * half) = w;
+    }
+  if (lse != nullptr && half == 0) lse[qi * HQ + hq] = (mf + log2f(Z)) * LN2;
+}
+
+// fp32 kernel: plain FMA arithmetic, one 64-row chunk of queries per
+// workgroup, 4 threads per query row; thread `sub` owns channels n = 4e + sub.
+template <int DK, int DV, bool HAS_GS>
+__global__ __launch_bounds__(256) void k_attn_fwd_f32(
+    const float *__restrict__ qh, const float *__restrict__ kt, const float *__restrict__ v,
+    const float *__restrict__ anch, const float *__restrict__ gsum,
+    const float *__restrict__ sink, float *__restrict__ o, float *__restrict__ lse,
+    const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int nseg, int NCmax, int NCH,
+    int64_t window) {
+  constexpr int QPT = DK / 4, VPT = DV / 4;
+  __shared__ float Ks[BN * DK];
+  __shared__ float Vs[BN * DV];
+  __shared__ float dL[DK];
+  __shared__ float Gj[BN];
+
+  const int tid = threadIdx.x;
+  const int hq = blockIdx.x % HQ;
+  const int rest = blockIdx.x / HQ;
+  const int seg = rest % nseg;
+  const int c = NCH - 1 - rest / nseg;
+  int64_t bos, eos;
+  segment_bounds(seg, T, cu, bos, eos);
+  const int64_t L = eos - bos;
+  const int nch = (int)((L + CHUNK - 1) / CHUNK);
+  if (c >= nch) return;
+  const int h = hq / (HQ / H);
+  const int64_t i0 = bos + (int64_t)c * CHUNK;
+  const int64_t i_last = min(i0 + CHUNK, eos) - 1;
+  const int64_t jlo_blk = window > 0 ? max(bos, i0 - window + 1) : bos;
+  const int Jlo = (int)((jlo_blk - bos) / BN), Jhi = c;
+
+  const int row = tid >> 2, sub = tid & 3;
+  const int64_t qi = i0 + row;
+  const bool q_ok = qi < eos;
+  float qv[QPT];
+#pragma unroll
+  for (int e = 0; e < QPT; ++e) qv[e] = q_ok ? qh[(qi * HQ + hq) * DK + 4 * e + sub] : 0.f;
+  const float g_i = (HAS_GS && q_ok) ? gsum[qi * HQ + hq] : 0.f;
+  const int64_t cbase = (int64_t)seg * NCmax;
+  const int cq = c & ~1;  // anchor of the first chunk of the 128-row query tile
+  const float RQ = tid < DK ? anch[((cbase + cq) * HQ + hq) * DK + tid] : 0.f;
+
+  float m_run = -INFINITY, l_run = 0.f;
+  float oacc[VPT];
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) oacc[e] = 0.f;
+
+  for (int J = Jlo; J <= Jhi; ++J) {
+    const int64_t kj0 = bos + (int64_t)J * BN;
+    __syncthreads();
+    if (tid < DK) dL[tid] = fast_exp2(RQ - anch[((cbase + J) * HQ + hq) * DK + tid]);
+    if (HAS_GS && tid < BN) Gj[tid] = kj0 + tid < eos ? gsum[(kj0 + tid) * HQ + hq] : 0.f;
+    __syncthreads();
+    for (int x = tid; x < BN * DK; x += 256) {
+      const int r = x / DK, n = x % DK;
+      Ks[x] = kj0 + r < eos ? kt[((kj0 + r) * HQ + hq) * DK + n] * dL[n] : 0.f;
+    }
+    for (int x = tid; x < BN * DV; x += 256) {
+      const int r = x / DV, n = x % DV;
+      Vs[x] = kj0 + r < eos ? v[((kj0 + r) * H + h) * DV + n] : 0.f;
+    }
+    __syncthreads();
+    float s[BN];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < QPT; ++e) part = fmaf(qv[e], Ks[jj * DK + 4 * e + sub], part);
+      part += __shfl_xor(part, 1);
+      part += __shfl_xor(part, 2);
+      const int64_t j = kj0 + jj;
+      if (HAS_GS) part += g_i - Gj[jj];
+      if (j > qi || j >= eos || (window > 0 && qi - j >= window)) part = -INFINITY;
+      s[jj] = part;
+      mx = fmaxf(mx, part);
+    }
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < BN; ++jj) {
+      s[jj] = fast_exp2(s[jj] - m_use);
+      rs += s[jj];
+    }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) {
+      float acc = oacc[e] * alpha;
+#pragma unroll
+      for (int jj = 0; jj < BN; ++jj) acc = fmaf(s[jj], Vs[jj * DV + 4 * e + sub], acc);
+      oacc[e] = acc;
+    }
+  }
+  (void)i_last;
+  if (!q_ok) return;
+  float mf = m_run, Z = l_run;
+  if (sink != nullptr) {
+    const float s2 = sink[hq] * LOG2E;
+    mf = fmaxf(m_run, s2);
+    Z = l_run * fast_exp2(m_run - mf) + fast_exp2(s2 - mf);
+  }
+  const float inv = fast_exp2(m_run - mf) / Z;
+#pragma unroll
+  for (int e = 0; e < VPT; ++e) o[(qi * HQ + hq) * DV + 4 * e + sub] = oacc[e] * inv;
+  if (lse != nullptr && sub == 0) lse[qi * HQ + hq] = (mf + log2f(Z)) * LN2;
+}
+
+template <int DK, int DV>
+hipError_t attn_bf16_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
+  const int NCmax = (int)((p.maxlen + CHUNK - 1) / CHUNK);
+  const int NQT = (int)((p.maxlen + QTILE - 1) / QTILE);
+  const dim3 grid((unsigned)(NQT * p.nseg * p.HQ));
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const _Float16 *>(ws.qh),
+                       static_cast<const _Float16 *>(ws.kt), static_cast<const bf16_t *>(p.v),
+                       ws.anch, ws.gsum, p.sink, static_cast<bf16_t *>(p.o), p.lse, p.cu, p.T,
+                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT, p.window);
+  };
+  if (p.g_scalar != nullptr)
+    args(k_attn_fwd_bf16<DK, DV, true>);
+  else
+    args(k_attn_fwd_bf16<DK, DV, false>);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+hipError_t attn_f32_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
+  const int NCmax = (int)((p.maxlen + CHUNK - 1) / CHUNK);
+  const dim3 grid((unsigned)(NCmax * p.nseg * p.HQ));
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const float *>(ws.qh),
+                       static_cast<const float *>(ws.kt), static_cast<const float *>(p.v),
+                       ws.anch, ws.gsum, p.sink, static_cast<float *>(p.o), p.lse, p.cu, p.T,
+                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NCmax, p.window);
+  };
+  if (p.g_scalar != nullptr)
+    args(k_attn_fwd_f32<DK, DV, true>);
+  else
+    args(k_attn_fwd_f32<DK, DV, false>);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
+  if (p.dtype == 0) {
+    if (p.K == 64) return p.V == 64 ? attn_bf16_t<64, 64>(p, ws, st) : attn_bf16_t<64, 128>(p, ws, st);
+    return p.V == 64 ? attn_bf16_t<128, 64>(p, ws, st) : attn_bf16_t<128, 128>(p, ws, st);
+  }
+  if (p.K == 64) return p.V == 64 ? attn_f32_t<64, 64>(p, ws, st) : attn_f32_t<64, 128>(p, ws, st);
+  return p.V == 64 ? attn_f32_t<128, 64>(p, ws, st) : attn_f32_t<128, 128>(p, ws, st);
+}
+
+}  // namespace wa

@@ -1,0 +1,402 @@
+// Running decay sums, chunk anchors and rescaled operands (the pre-pass of
+// the prefill and the decode-cache build).
+//
+// Wall Attention README, "Decode": the prefix P of g is taken in log2 units
+// (scale 1/ln 2), and per-chunk anchors R_c fold the decay into the keys,
+// k_tilde[j] = k[j] * 2^(R_c - P[j]), keeping every exp2 argument bounded
+// ("Features": numerically stable long context).  The same factorisation
+// serves the prefill: for query i in query tile I and key j in key chunk J,
+//   exp(P_i - P_j) = 2^(P2_i - RQ_I) * 2^(RQ_I - R_J) * 2^(R_J - P2_j)
+// exactly, so this pass writes q_hat_i = q_i * 2^(P2_i - RQ_I) * scale/ln2 and
+// k_tilde_j = k_j * 2^(R_J - P2_j) once per token, and the attention kernel
+// multiplies one 64-key tile by the K factors 2^(RQ_I - R_J) per tile pair.
+//
+// The running sum along time is a three-phase chunked scan:
+//   A: per-chunk channel sums,  B: exclusive scan over chunks,  C: in-chunk
+//   inclusive sums plus the operand rescaling.
+#include "common.h"
+#include "launch.h"
+
+namespace wa {
+
+namespace {
+
+template <typename TE>
+__device__ __forceinline__ float4 load4(const TE *p);
+template <>
+__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t *p) {
+  u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+  return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+}
+template <>
+__device__ __forceinline__ float4 load4<float>(const float *p) {
+  return *reinterpret_cast<const float4 *>(p);
+}
+template <typename TE>
+__device__ __forceinline__ void store4(TE *p, float4 x);
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t *p, float4 x) {
+  u32x2 w;
+  w.x = pack_bf16x2(x.x, x.y);
+  w.y = pack_bf16x2(x.z, x.w);
+  *reinterpret_cast<u32x2 *>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16 *p, float4 x) {
+  u32x2 w;
+  w.x = pack_f16x2(x.x, x.y);
+  w.y = pack_f16x2(x.z, x.w);
+  *reinterpret_cast<u32x2 *>(p) = w;
+}
+template <>
+__device__ __forceinline__ void store4<float>(float *p, float4 x) {
+  *reinterpret_cast<float4 *>(p) = x;
+}
+
+__device__ __forceinline__ float wave_inclusive_scan(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    float y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// Phase A: sum of g (per channel) and of g_scalar over each chunk.
+// grid (NCmax, HQ, nseg), 256 threads.
+template <typename TE, int KD>
+__global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
+                                                    const TE *__restrict__ gs,
+                                                    float *__restrict__ csum,
+                                                    float *__restrict__ csum_s,
+                                                    const int32_t *__restrict__ cu, int64_t T,
+                                                    int HQ, int NCmax) {
+  const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
+  int64_t bos, eos;
+  segment_bounds(s, T, cu, bos, eos);
+  const int64_t r0 = bos + (int64_t)c * CHUNK;
+  if (r0 >= eos) return;
+  const int nrow = (int)min<int64_t>(CHUNK, eos - r0);
+  constexpr int NG = 256 / KD;
+  const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
+  float acc = 0.f;
+  for (int r = grp; r < nrow; r += NG) acc += Elem<TE>::ld(g + ((r0 + r) * HQ + hq) * KD + n);
+  __shared__ float red[256];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  const int64_t cidx = (int64_t)s * NCmax + c;
+  if (grp == 0) {
+#pragma unroll
+    for (int q = 1; q < NG; ++q) acc += red[q * KD + n];
+    csum[(cidx * HQ + hq) * KD + n] = acc;
+  }
+  if (gs != nullptr && threadIdx.x < 64) {
+    float a = (int)threadIdx.x < nrow ? Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.f;
+    a = wave_sum(a);
+    if (threadIdx.x == 0) csum_s[cidx * HQ + hq] = a;
+  }
+}
+
+// Phase B: exclusive scan of the chunk sums along time (in place), and the
+// chunk anchors anch[c] = (offset + sum of chunk c) * log2(e) = P2 at the
+// chunk's last token.  Channel index KD stands for g_scalar.
+// grid (HQ, nseg, ceil((KD+1)/32)), 256 threads = 32 channels x 8 chunk groups.
+template <int KD>
+__global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
+                                                    float *__restrict__ anch,
+                                                    float *__restrict__ csum_s,
+                                                    const int32_t *__restrict__ cu, int64_t T,
+                                                    int HQ, int NCmax, int with_gs) {
+  const int hq = blockIdx.x, s = blockIdx.y;
+  const int ch = blockIdx.z * 32 + (threadIdx.x & 31);
+  const int grp = threadIdx.x >> 5;
+  int64_t bos, eos;
+  segment_bounds(s, T, cu, bos, eos);
+  const int nch = (int)((eos - bos + CHUNK - 1) / CHUNK);
+  const bool active = ch < KD || (ch == KD && with_gs);
+  const int span = (nch + 7) / 8;
+  const int cb = grp * span, ce = min(nch, cb + span);
+  float *p;
+  int64_t stride;
+  const int64_t c0 = (int64_t)s * NCmax;
+  if (ch < KD) {
+    p = csum + (c0 * HQ + hq) * KD + ch;
+    stride = (int64_t)HQ * KD;
+  } else {
+    p = csum_s + c0 * HQ + hq;
+    stride = HQ;
+  }
+  float tot = 0.f;
+  if (active)
+    for (int c = cb; c < ce; ++c) tot += p[c * stride];
+  __shared__ float part[8][32];
+  part[grp][threadIdx.x & 31] = tot;
+  __syncthreads();
+  if (!active) return;
+  float run = 0.f;
+  for (int q = 0; q < grp; ++q) run += part[q][threadIdx.x & 31];
+  float *a = anch + (c0 * HQ + hq) * KD + ch;
+  for (int c = cb; c < ce; ++c) {
+    const float x = p[c * stride];
+    p[c * stride] = run;
+    if (ch < KD) a[c * stride] = (run + x) * LOG2E;
+    run += x;
+  }
+}
+
+// Phase C for the prefill: in-chunk running sums, then
+//   q_hat = q * 2^(P2 - RQ) * qscale   (RQ: anchor of the first chunk of the
+//                                       128-row query tile, so |P2 - RQ| is
+//                                       at most one chunk's decay span)
+//   k_tilde = k * 2^(R_c - P2)         (R_c: anchor of this 64-token chunk)
+// written in the operand type (IEEE half for bf16 inputs, float for fp32).
+//   gsum = running sum of g_scalar in log2 units.
+// grid (NCmax, HQ, nseg), 256 threads.
+template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
+__global__ __launch_bounds__(256) void k_prefill_operands(
+    const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ g,
+    const TE *__restrict__ gs, const float *__restrict__ off, const float *__restrict__ anch,
+    const float *__restrict__ off_s, TO *__restrict__ qh, TO *__restrict__ kt,
+    float *__restrict__ gsum, const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int NCmax,
+    float qscale) {
+  const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
+  int64_t bos, eos;
+  segment_bounds(s, T, cu, bos, eos);
+  const int64_t r0 = bos + (int64_t)c * CHUNK;
+  if (r0 >= eos) return;
+  const int nrow = (int)min<int64_t>(CHUNK, eos - r0);
+  const int h = hq / (HQ / H);
+  constexpr int NG = 256 / KD;
+  constexpr int RPG = CHUNK / NG;
+  const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
+  float gv[RPG];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    const int r = grp * RPG + i;
+    gv[i] = r < nrow ? Elem<TE>::ld(g + ((r0 + r) * HQ + hq) * KD + n) : 0.f;
+  }
+#pragma unroll
+  for (int i = 1; i < RPG; ++i) gv[i] += gv[i - 1];
+  __shared__ float tot[NG][KD];
+  tot[grp][n] = gv[RPG - 1];
+  __syncthreads();
+  const int64_t cidx = (int64_t)s * NCmax + c;
+  const int64_t cq = (int64_t)s * NCmax + (c & ~1);
+  float base = off[(cidx * HQ + hq) * KD + n];
+  for (int q2 = 0; q2 < grp; ++q2) base += tot[q2][n];
+  const float A = anch[(cidx * HQ + hq) * KD + n];
+  const float RQ = anch[(cq * HQ + hq) * KD + n];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    const int r = grp * RPG + i;
+    if (r < nrow) {
+      const int64_t t = r0 + r;
+      const float P2 = (base + gv[i]) * LOG2E;
+      const float qv = Elem<TE>::ld(q + (t * HQ + hq) * KD + n);
+      const float kv = Elem<TE>::ld(k + (t * H + h) * KD + n);
+      Elem<TO>::st(qh + (t * HQ + hq) * KD + n, qv * fast_exp2(P2 - RQ) * qscale);
+      Elem<TO>::st(kt + (t * HQ + hq) * KD + n, kv * fast_exp2(A - P2));
+    }
+  }
+  if (gs != nullptr && threadIdx.x < 64) {
+    const int r = threadIdx.x;
+    float x = r < nrow ? Elem<TE>::ld(gs + (r0 + r) * HQ + hq) : 0.f;
+    x = wave_inclusive_scan(x);
+    if (r < nrow) gsum[(r0 + r) * HQ + hq] = (off_s[cidx * HQ + hq] + x) * LOG2E;
+  }
+}
+
+// Phase C for the stand-alone prefix: P2 = (offset + in-chunk sum) * log2(e).
+template <typename TE, int KD>
+__global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
+                                                      const float *__restrict__ off,
+                                                      float *__restrict__ P2,
+                                                      const int32_t *__restrict__ cu, int64_t T,
+                                                      int HQ, int NCmax) {
+  const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
+  int64_t bos, eos;
+  segment_bounds(s, T, cu, bos, eos);
+  const int64_t r0 = bos + (int64_t)c * CHUNK;
+  if (r0 >= eos) return;
+  const int nrow = (int)min<int64_t>(CHUNK, eos - r0);
+  constexpr int NG = 256 / KD;
+  constexpr int RPG = CHUNK / NG;
+  const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
+  float gv[RPG];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    const int r = grp * RPG + i;
+    gv[i] = r < nrow ? Elem<TE>::ld(g + ((r0 + r) * HQ + hq) * KD + n) : 0.f;
+  }
+#pragma unroll
+  for (int i = 1; i < RPG; ++i) gv[i] += gv[i - 1];
+  __shared__ float tot[NG][KD];
+  tot[grp][n] = gv[RPG - 1];
+  __syncthreads();
+  const int64_t cidx = (int64_t)s * NCmax + c;
+  float base = off[(cidx * HQ + hq) * KD + n];
+  for (int q2 = 0; q2 < grp; ++q2) base += tot[q2][n];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    const int r = grp * RPG + i;
+    if (r < nrow) P2[((r0 + r) * HQ + hq) * KD + n] = (base + gv[i]) * LOG2E;
+  }
+}
+
+// Decode cache: r_cache[c] = P2 at the chunk's last token (copied), and
+// k_tilde = k * 2^(r_cache[c] - P2) in the operand type.  grid (NC, HQ, B),
+// 256 threads; each thread owns 4 channels.
+template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
+__global__ __launch_bounds__(256) void k_build_cache(const TE *__restrict__ k,
+                                                     const float *__restrict__ P2,
+                                                     TO *__restrict__ kt, float *__restrict__ rc,
+                                                     int64_t T, int HQ, int H, int NC) {
+  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+  const int64_t r0 = (int64_t)c * CHUNK;
+  const int nrow = (int)min<int64_t>(CHUNK, T - r0);
+  const int h = hq / (HQ / H);
+  constexpr int NQ = KD / 4;
+  constexpr int NRG = 256 / NQ;
+  const int n4 = (threadIdx.x % NQ) * 4, rg = threadIdx.x / NQ;
+  const int64_t tb = (int64_t)b * T;
+  const float4 R =
+      *reinterpret_cast<const float4 *>(P2 + ((tb + r0 + nrow - 1) * HQ + hq) * KD + n4);
+  if (rg == 0)
+    *reinterpret_cast<float4 *>(rc + (((int64_t)b * NC + c) * HQ + hq) * KD + n4) = R;
+  for (int r = rg; r < nrow; r += NRG) {
+    const int64_t t = tb + r0 + r;
+    const float4 p = *reinterpret_cast<const float4 *>(P2 + (t * HQ + hq) * KD + n4);
+    const float4 kv = load4<TE>(k + (t * H + h) * KD + n4);
+    float4 out;
+    out.x = kv.x * fast_exp2(R.x - p.x);
+    out.y = kv.y * fast_exp2(R.y - p.y);
+    out.z = kv.z * fast_exp2(R.z - p.z);
+    out.w = kv.w * fast_exp2(R.w - p.w);
+    store4<TO>(kt + (t * HQ + hq) * KD + n4, out);
+  }
+}
+
+template <typename TE, int KD>
+hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
+  typedef typename OperandOf<TE>::type TO;
+  const int NCmax = (int)((p.maxlen + CHUNK - 1) / CHUNK);
+  const dim3 gridA(NCmax, (unsigned)p.HQ, (unsigned)p.nseg);
+  const TE *gs = static_cast<const TE *>(p.g_scalar);
+  hipLaunchKernelGGL((k_chunk_sums<TE, KD>), gridA, dim3(256), 0, st,
+                     static_cast<const TE *>(p.g), gs, ws.csum, ws.csum_s, p.cu, p.T, (int)p.HQ,
+                     NCmax);
+  const dim3 gridB((unsigned)p.HQ, (unsigned)p.nseg, (KD + 1 + 31) / 32);
+  hipLaunchKernelGGL((k_chunk_scan<KD>), gridB, dim3(256), 0, st, ws.csum, ws.anch, ws.csum_s,
+                     p.cu, p.T, (int)p.HQ, NCmax, gs != nullptr ? 1 : 0);
+  const float qscale = p.scale * LOG2E;
+  hipLaunchKernelGGL((k_prefill_operands<TE, KD>), gridA, dim3(256), 0, st,
+                     static_cast<const TE *>(p.q), static_cast<const TE *>(p.k),
+                     static_cast<const TE *>(p.g), gs, ws.csum, ws.anch, ws.csum_s,
+                     static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt), ws.gsum, p.cu, p.T,
+                     (int)p.HQ, (int)p.H, NCmax, qscale);
+  return hipGetLastError();
+}
+
+template <typename TE, int KD>
+hipError_t prefix_log2_t(const void *g, float *P2, const int32_t *cu, int64_t T, int64_t HQ,
+                         int64_t nseg, int64_t maxlen, float *csum, hipStream_t st) {
+  const int NCmax = (int)((maxlen + CHUNK - 1) / CHUNK);
+  const dim3 gridA(NCmax, (unsigned)HQ, (unsigned)nseg);
+  hipLaunchKernelGGL((k_chunk_sums<TE, KD>), gridA, dim3(256), 0, st,
+                     static_cast<const TE *>(g), (const TE *)nullptr, csum, (float *)nullptr, cu,
+                     T, (int)HQ, NCmax);
+  // The anchors of phase B are not needed here; they go to the upper half of
+  // the workspace, which prefix_workspace_layout reserves for them.
+  float *anch = csum + (int64_t)nseg * NCmax * HQ * KD;
+  const dim3 gridB((unsigned)HQ, (unsigned)nseg, KD / 32);
+  hipLaunchKernelGGL((k_chunk_scan<KD>), gridB, dim3(256), 0, st, csum, anch, (float *)nullptr,
+                     cu, T, (int)HQ, NCmax, 0);
+  hipLaunchKernelGGL((k_prefix_write<TE, KD>), gridA, dim3(256), 0, st,
+                     static_cast<const TE *>(g), csum, P2, cu, T, (int)HQ, NCmax);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
+  const int64_t NCmax = (p.maxlen + CHUNK - 1) / CHUNK;
+  const int64_t nchunk = p.nseg * NCmax;
+  const size_t esz = p.dtype == 0 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *ptr = base ? base + off : nullptr;
+    off += align256(bytes);
+    return ptr;
+  };
+  char *csum = take(sizeof(float) * nchunk * p.HQ * p.K);
+  char *anch = take(sizeof(float) * nchunk * p.HQ * p.K);
+  char *csum_s = take(sizeof(float) * nchunk * p.HQ);
+  char *qh = take(esz * p.ntok * p.HQ * p.K);
+  char *kt = take(esz * p.ntok * p.HQ * p.K);
+  char *gsum = take(sizeof(float) * p.ntok * p.HQ);
+  if (ws) {
+    ws->csum = reinterpret_cast<float *>(csum);
+    ws->anch = reinterpret_cast<float *>(anch);
+    ws->csum_s = reinterpret_cast<float *>(csum_s);
+    ws->qh = qh;
+    ws->kt = kt;
+    ws->gsum = reinterpret_cast<float *>(gsum);
+  }
+  return off;
+}
+
+size_t prefix_workspace_layout(int64_t nseg, int64_t maxlen, int64_t HQ, int64_t K, float **csum,
+                               char *base) {
+  const int64_t NCmax = (maxlen + CHUNK - 1) / CHUNK;
+  if (csum) *csum = reinterpret_cast<float *>(base);
+  return align256(2 * sizeof(float) * nseg * NCmax * HQ * K);
+}
+
+hipError_t launch_prefix_phases(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
+  if (p.dtype == 0) {
+    return p.K == 64 ? prefix_phases_t<bf16_t, 64>(p, ws, st) : prefix_phases_t<bf16_t, 128>(p, ws, st);
+  }
+  return p.K == 64 ? prefix_phases_t<float, 64>(p, ws, st) : prefix_phases_t<float, 128>(p, ws, st);
+}
+
+hipError_t launch_prefix_log2(const void *g, float *P2, const int32_t *cu, int64_t T, int64_t HQ,
+                              int64_t K, int64_t nseg, int64_t maxlen, int dtype, float *csum,
+                              hipStream_t st) {
+  if (dtype == 0)
+    return K == 64 ? prefix_log2_t<bf16_t, 64>(g, P2, cu, T, HQ, nseg, maxlen, csum, st)
+                   : prefix_log2_t<bf16_t, 128>(g, P2, cu, T, HQ, nseg, maxlen, csum, st);
+  return K == 64 ? prefix_log2_t<float, 64>(g, P2, cu, T, HQ, nseg, maxlen, csum, st)
+                 : prefix_log2_t<float, 128>(g, P2, cu, T, HQ, nseg, maxlen, csum, st);
+}
+
+hipError_t launch_build_cache(const void *k, const float *P2, void *kt, float *rc, int64_t B,
+                              int64_t T, int64_t HQ, int64_t H, int64_t K, int dtype,
+                              hipStream_t st) {
+  const int NC = (int)((T + CHUNK - 1) / CHUNK);
+  const dim3 grid(NC, (unsigned)HQ, (unsigned)B);
+  if (dtype == 0) {
+    if (K == 64)
+      hipLaunchKernelGGL((k_build_cache<bf16_t, 64>), grid, dim3(256), 0, st,
+                         static_cast<const bf16_t *>(k), P2, static_cast<_Float16 *>(kt), rc, T,
+                         (int)HQ, (int)H, NC);
+    else
+      hipLaunchKernelGGL((k_build_cache<bf16_t, 128>), grid, dim3(256), 0, st,
+                         static_cast<const bf16_t *>(k), P2, static_cast<_Float16 *>(kt), rc, T,
+                         (int)HQ, (int)H, NC);
+  } else {
+    if (K == 64)
+      hipLaunchKernelGGL((k_build_cache<float, 64>), grid, dim3(256), 0, st,
+                         static_cast<const float *>(k), P2, static_cast<float *>(kt), rc, T,
+                         (int)HQ, (int)H, NC);
+    else
+      hipLaunchKernelGGL((k_build_cache<float, 128>), grid, dim3(256), 0, st,
+                         static_cast<const float *>(k), P2, static_cast<float *>(kt), rc, T,
+                         (int)HQ, (int)H, NC);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace wa

@@ -1,0 +1,127 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any launch.
+
+The argument checks only exercise paths that return before the first HIP
+call, so they run on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wallattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import exact_attention_channel_amd as wa
+    if not os.path.exists(wa.library_path()):
+        from exact_attention_channel_amd import build
+        build.build()
+    return wa.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(wall_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("wall_attn_fwd", "wall_attn_build_kv_cache", "wall_attn_decode",
+              "wall_attn_prefix_log2", "wall_attn_last_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    import exact_attention_channel_amd as wa
+    names = declared_functions()
+    assert set(names) == set(wa.EXPORTED_SYMBOLS)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", wa.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def fwd(lib, B=1, T=128, HQ=4, H=2, K=64, V=64, cu=None, nseq=0, maxlen=0, dtype=0,
+        ws_bytes=1 << 40, q=FAKE, k=FAKE, v=FAKE, g=FAKE, o=FAKE, ws=FAKE, gs=None):
+    return lib.wall_attn_fwd(q, k, v, g, gs, None, o, None, B, T, HQ, H, K, V, cu, nseq, maxlen,
+                             0, 0.0, dtype, ws, ws_bytes, None)
+
+
+def test_fwd_rejects_bad_shapes(lib):
+    assert fwd(lib, HQ=6, H=4) == 1                       # HQ % H != 0
+    assert b"multiple" in lib.wall_attn_last_error()
+    assert fwd(lib, B=2, cu=FAKE, nseq=2, maxlen=64) == 1   # cu_seqlens needs B == 1
+    assert fwd(lib, B=0) == 1
+    assert fwd(lib, T=-5) == 1
+    assert fwd(lib, K=96) == 2
+    assert fwd(lib, V=256) == 2
+    assert fwd(lib, dtype=7) == 2
+    assert fwd(lib, cu=FAKE, nseq=0, maxlen=64) == 1
+    assert fwd(lib, cu=FAKE, nseq=2, maxlen=500) == 1       # max_seqlen > T
+
+
+def test_fwd_rejects_bad_pointers_and_workspace(lib):
+    assert fwd(lib, q=None) == 1
+    assert fwd(lib, o=None) == 1
+    assert fwd(lib, ws=None) == 1
+    assert fwd(lib, k=FAKE + 2) == 1                        # misaligned
+    assert fwd(lib, gs=FAKE + 8) == 1
+    need = lib.wall_attn_fwd_workspace_bytes(1, 128, 4, 2, 64, 64, 0, 0, 0)
+    assert need > 0
+    assert fwd(lib, ws_bytes=need - 1) == 4
+    assert b"workspace" in lib.wall_attn_last_error()
+
+
+def test_workspace_sizes(lib):
+    assert lib.wall_attn_fwd_workspace_bytes(1, 128, 4, 3, 64, 64, 0, 0, 0) == 0
+    a = lib.wall_attn_fwd_workspace_bytes(1, 8192, 16, 4, 128, 128, 0, 0, 0)
+    b = lib.wall_attn_fwd_workspace_bytes(1, 8192, 16, 4, 128, 128, 0, 0, 1)
+    # rescaled q and k dominate: 2 * T * HQ * K elements
+    assert a >= 2 * 8192 * 16 * 128 * 2 and b >= 2 * 8192 * 16 * 128 * 4 and b > a
+    assert lib.wall_attn_decode_workspace_bytes(64, 32768, 32, 8, 128, 128, 64) > 0
+    assert lib.wall_attn_decode_workspace_bytes(64, 32768, 32, 8, 128, 128, 32) == 0
+    assert lib.wall_attn_prefix_log2_workspace_bytes(2, 100, 4, 64, 0, 0) > 0
+
+
+def test_cache_and_decode_reject_bad_arguments(lib):
+    bk = lib.wall_attn_build_kv_cache
+    assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 32, 0, None) == 2   # chunk_size
+    assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 3, 64, 64, 0, None) == 1   # HQ % H
+    assert bk(None, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 64, 0, None) == 1
+    assert bk(FAKE, FAKE, FAKE + 4, FAKE, 1, 128, 4, 2, 64, 64, 0, None) == 1
+    dec = lib.wall_attn_decode
+
+    def d(**kw):
+        a = dict(q=FAKE, v=FAKE, p=FAKE, kt=FAKE, r=FAKE, s=None, o=FAKE, l=None, B=2, T=256,
+                 HQ=8, H=2, K=128, V=128, C=64, scale=0.0, dt=0, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return dec(a["q"], a["v"], a["p"], a["kt"], a["r"], a["s"], a["o"], a["l"], a["B"],
+                   a["T"], a["HQ"], a["H"], a["K"], a["V"], a["C"], a["scale"], a["dt"], a["ws"],
+                   a["wsb"], None)
+    assert d(C=128) == 2
+    assert d(HQ=6, H=4) == 1
+    assert d(K=80) == 2
+    assert d(kt=None) == 1
+    assert d(o=FAKE + 2) == 1
+    assert d(wsb=16) == 4
+    assert d(dt=3) == 2
+
+
+def test_python_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import exact_attention_channel_amd as wa
+    x = torch.zeros(1, 64, 2, 64)
+    with pytest.raises(ValueError):
+        wa.wall_attn(x, x[:, :, :1], x[:, :, :1], x)
