@@ -48,47 +48,53 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
     const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int nseg, int NCmax, int NQT,
-    int64_t window) {
+    int window) {
   constexpr int KS = DK + 8;  // LDS row stride (elements) of the key tile
   constexpr int VS = BN + 8;  // LDS row stride (elements) of the transposed value tile
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KS];  // half bits
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[DV * VS];
-  __shared__ float Gj[BN];
+  // double-buffered tiles: one barrier per key tile
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];  // half bits
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DV * VS];
+  __shared__ __attribute__((aligned(16))) float Gj[2][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hq = blockIdx.x % HQ;
   const int rest = blockIdx.x / HQ;
   const int seg = rest % nseg;
   const int I = NQT - 1 - rest / nseg;  // longest query tiles first
-  int64_t bos, eos;
-  segment_bounds(seg, T, cu, bos, eos);
-  const int64_t L = eos - bos;
-  const int nqt = (int)((L + QTILE - 1) / QTILE);
+  int64_t bos64, eos64;
+  segment_bounds(seg, T, cu, bos64, eos64);
+  const int L = (int)(eos64 - bos64);  // sequence length; positions below are relative to bos
+  const int nqt = (L + QTILE - 1) / QTILE;
   if (I >= nqt) return;
   const int h = hq / (HQ / H);
-  const int64_t i0 = bos + (int64_t)I * QTILE;
-  const int64_t i_last = min(i0 + QTILE, eos) - 1;
-  const int64_t jlo_blk = window > 0 ? max(bos, i0 - window + 1) : bos;
-  const int Jlo = (int)((jlo_blk - bos) / BN), Jhi = (int)((i_last - bos) / BN);
+  const int i0 = I * QTILE;
+  const int i_last = min(i0 + QTILE, L) - 1;
+  const int jlo_blk = window > 0 ? max(0, i0 - window + 1) : 0;
+  const int Jlo = jlo_blk / BN, Jhi = i_last / BN;
 
-  const int64_t qw0 = i0 + wave * WROWS;
-  const bool wave_live = qw0 < eos;
-  const int64_t qw_last = min(qw0 + WROWS, eos) - 1;
-  const int64_t jw_lo = window > 0 ? max(bos, qw0 - window + 1) : bos;
+  const int qw0 = i0 + wave * WROWS;
+  const bool wave_live = qw0 < L;
+  const int qw_last = min(qw0 + WROWS, L) - 1;
+  const int jw_lo = window > 0 ? max(0, qw0 - window + 1) : 0;
 
   const int col = lane & 31, half = lane >> 5;
-  const int64_t qi = qw0 + col;
-  const bool q_ok = qi < eos;
+  const int qi = qw0 + col;
+  const bool q_ok = qi < L;
+
+  // per-head bases (token strides: HQ*DK for q_hat/k_tilde, H*DV for v)
+  const _Float16 *qh_b = qh + (bos64 * HQ + hq) * DK;
+  const _Float16 *kt_b = kt + (bos64 * HQ + hq) * DK;
+  const bf16_t *v_b = v + (bos64 * H + h) * DV;
+  const float *gs_b = HAS_GS ? gsum + bos64 * HQ + hq : nullptr;
+  const int qrow = HQ * DK, vrow = H * DV;
 
   f16x8 qB[DK / 16];
 #pragma unroll
   for (int ks = 0; ks < DK / 16; ++ks) {
-    if (q_ok)
-      qB[ks] = *reinterpret_cast<const f16x8 *>(qh + (qi * HQ + hq) * DK + ks * 16 + half * 8);
-    else
-      qB[ks] = f16x8{};
+    const int r = q_ok ? qi : L - 1;
+    qB[ks] = *reinterpret_cast<const f16x8 *>(qh_b + r * qrow + ks * 16 + half * 8);
   }
-  const float g_i = (HAS_GS && q_ok) ? gsum[qi * HQ + hq] : 0.f;
+  const float g_i = (HAS_GS && q_ok) ? gs_b[qi * HQ] : 0.f;
 
   // staging roles
   constexpr int KCP = DK / 8;      // 16-byte pieces per key row
@@ -114,59 +120,64 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
 
   u32x4 kreg[KNP];
   u32x4 vreg[4];
-  float dreg[8];
+  uint32_t dpk[4];       // per-channel-pair decay factors, exact powers of two in half
+  float csig_next = 1.f;  // 2^sigma of the tile held in registers
   float gj_reg = 0.f;
-  float csig_next = 1.f;  // 2^sigma of the tile being loaded
 
   auto load_tile = [&](int J) {
-    const int64_t kj0 = bos + (int64_t)J * BN;
+    const int kj0 = J * BN;
+    const bool full = kj0 + BN <= L;
+    const _Float16 *kb = kt_b + kj0 * qrow;
+#pragma unroll
+    for (int p = 0; p < KNP; ++p) {
+      int r = kr + p * KRP;
+      if (!full) r = min(r, L - 1 - kj0);  // rows past the end are masked; keep reads in bounds
+      kreg[p] = *reinterpret_cast<const u32x4 *>(kb + r * qrow + cp * 8);
+    }
+    if (v_role) {
+      const bf16_t *vb = v_b + kj0 * vrow + cg * 8;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        int rr = 4 * kq + r;
+        if (!full) rr = min(rr, L - 1 - kj0);
+        vreg[r] = *reinterpret_cast<const u32x4 *>(vb + rr * vrow);
+      }
+    }
+    if (HAS_GS && tid < BN) gj_reg = gs_b[min(kj0 + tid, L - 1) * HQ];
+    // d_IJ = 2^(RQ - R_J): the prefill anchors are integers, so the exponents
+    // are exact integers and the factors exact powers of two
     const float *ap = anch + ((cbase + J) * HQ + hq) * DK + cp * 8;
     const float4 a0 = *reinterpret_cast<const float4 *>(ap);
     const float4 a1 = *reinterpret_cast<const float4 *>(ap + 4);
-    dreg[0] = RQ[0] - a0.x; dreg[1] = RQ[1] - a0.y; dreg[2] = RQ[2] - a0.z; dreg[3] = RQ[3] - a0.w;
-    dreg[4] = RQ[4] - a1.x; dreg[5] = RQ[5] - a1.y; dreg[6] = RQ[6] - a1.z; dreg[7] = RQ[7] - a1.w;
-    // largest log2 factor over all channels: every group of KCP consecutive
-    // lanes holds all channel pieces
-    float emax = dreg[0];
+    float e[8] = {RQ[0] - a0.x, RQ[1] - a0.y, RQ[2] - a0.z, RQ[3] - a0.w,
+                  RQ[4] - a1.x, RQ[5] - a1.y, RQ[6] - a1.z, RQ[7] - a1.w};
+    float emax = fmaxf(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])),
+                       fmaxf(fmaxf(e[4], e[5]), fmaxf(e[6], e[7])));
 #pragma unroll
-    for (int e = 1; e < 8; ++e) emax = fmaxf(emax, dreg[e]);
+    for (int o2 = 1; o2 < KCP; o2 <<= 1) emax = fmaxf(emax, __shfl_xor(emax, o2));
+    // keep the staged half operands below 2^8 * |k_tilde|; scores are scaled back by 2^sigma
+    const int sigma = emax > 8.f ? (int)emax - 8 : 0;
+    csig_next = __builtin_amdgcn_ldexpf(1.f, sigma);
 #pragma unroll
-    for (int o = 1; o < KCP; o <<= 1) emax = fmaxf(emax, __shfl_xor(emax, o));
-    const float sigma = emax > 8.f ? ceilf(emax - 8.f) : 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) dreg[e] -= sigma;
-    csig_next = fast_exp2(sigma);
-#pragma unroll
-    for (int p = 0; p < KNP; ++p) {
-      const int64_t row = kj0 + kr + p * KRP;
-      kreg[p] = row < eos ? *reinterpret_cast<const u32x4 *>(kt + (row * HQ + hq) * DK + cp * 8)
-                          : u32x4{0, 0, 0, 0};
-    }
-    if (v_role) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = kj0 + 4 * kq + r;
-        vreg[r] = row < eos ? *reinterpret_cast<const u32x4 *>(v + (row * H + h) * DV + cg * 8)
-                            : u32x4{0, 0, 0, 0};
-      }
-    }
-    if (HAS_GS && tid < BN) {
-      const int64_t row = kj0 + tid;
-      gj_reg = row < eos ? gsum[row * HQ + hq] : 0.f;
+    for (int w = 0; w < 4; ++w) {
+      const int e0 = max((int)e[2 * w] - sigma, -30), e1 = max((int)e[2 * w + 1] - sigma, -30);
+      dpk[w] = pack_f16x2(__builtin_amdgcn_ldexpf(1.f, e0), __builtin_amdgcn_ldexpf(1.f, e1));
     }
   };
 
-  auto store_tile = [&]() {
-    float d[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) d[e] = fast_exp2(dreg[e]);
+  auto store_tile = [&](int buf) {
 #pragma unroll
     for (int p = 0; p < KNP; ++p) {
-      u32x4 w = kreg[p], out;
+      u32x4 out;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        out[e] = pack_f16x2(f16_lo(w[e]) * d[2 * e], f16_hi(w[e]) * d[2 * e + 1]);
-      *reinterpret_cast<u32x4 *>(&Ks[(kr + p * KRP) * KS + cp * 8]) = out;
+      for (int w = 0; w < 4; ++w) {
+        // copy the vector element to a scalar first: bit-casting the element
+        // expression directly has been seen to read element 0
+        const uint32_t kw = kreg[p][w], dw = dpk[w];
+        const f16x2 prod = __builtin_bit_cast(f16x2, kw) * __builtin_bit_cast(f16x2, dw);
+        out[w] = __builtin_bit_cast(uint32_t, prod);
+      }
+      *reinterpret_cast<u32x4 *>(&Ks[buf][(kr + p * KRP) * KS + cp * 8]) = out;
     }
     if (v_role) {
 #pragma unroll
@@ -180,109 +191,137 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
           out.x = (vreg[0][wi] & 0xffffu) | (vreg[1][wi] << 16);
           out.y = (vreg[2][wi] & 0xffffu) | (vreg[3][wi] << 16);
         }
-        *reinterpret_cast<u32x2 *>(&Vt[(cg * 8 + c) * VS + vpos]) = out;
+        *reinterpret_cast<u32x2 *>(&Vt[buf][(cg * 8 + c) * VS + vpos]) = out;
       }
     }
-    if (HAS_GS && tid < BN) Gj[tid] = gj_reg;
+    if (HAS_GS && tid < BN) Gj[buf][tid] = gj_reg;
   };
 
+  // Online softmax state of this lane's query (log2 units).  The running max
+  // is raised only when a tile's max exceeds it by more than 2^8 (exp2 of the
+  // scores stays below 256, far inside fp32 and bf16 range), so the output
+  // accumulators are rescaled rarely.
+  constexpr float TAU = 8.f;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 oacc[DV / 32];
 #pragma unroll
   for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = f32x16{};
 
   load_tile(Jlo);
-  store_tile();
-  float csig = csig_next;  // 2^sigma of the tile in LDS
-  for (int J = Jlo; J <= Jhi; ++J) {
-    __syncthreads();
-    if (J < Jhi) load_tile(J + 1);
-    const int64_t kj0 = bos + (int64_t)J * BN;
+  store_tile(Jlo & 1);
+  float csig_cur = csig_next;  // 2^sigma of the tile being computed
+  float csig_stg = 1.f;        // 2^sigma of the tile staged in the other buffer
+  if (Jlo < Jhi) load_tile(Jlo + 1);
+  const int rel0 = qi - 4 * half;  // query position minus this lane's key sub-offset
+
+  for (int J = Jlo; J <= Jhi; ++J, csig_cur = csig_stg) {
+    const int buf = J & 1;
+    __syncthreads();  // tile J is in LDS; every wave has finished reading the other buffer
+    if (J < Jhi) {
+      store_tile(buf ^ 1);
+      csig_stg = csig_next;
+      if (J + 1 < Jhi) load_tile(J + 2);
+    }
+    const int kj0 = J * BN;
     const bool need = wave_live && kj0 <= qw_last && kj0 + BN - 1 >= jw_lo;
-    if (need) {
-      f32x16 S[2];
+    if (!need) continue;
+    f32x16 S[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        S[sb] = f32x16{};
+    for (int sb = 0; sb < 2; ++sb) {
+      S[sb] = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < DK / 16; ++ks) {
-          const f16x8 a =
-              *reinterpret_cast<const f16x8 *>(&Ks[(sb * 32 + col) * KS + ks * 16 + half * 8]);
-          S[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[ks], S[sb], 0, 0, 0);
-        }
+      for (int ks = 0; ks < DK / 16; ++ks) {
+        const f16x8 a =
+            *reinterpret_cast<const f16x8 *>(&Ks[buf][(sb * 32 + col) * KS + ks * 16 + half * 8]);
+        S[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[ks], S[sb], 0, 0, 0);
       }
-      const bool masked =
-          (kj0 + BN - 1 > qw0) || (window > 0 && qw0 + WROWS - 1 - kj0 >= window);
-      float cs = csig;  // scores are S * cs until folded in below
-      if (HAS_GS || masked) {
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int kk = sb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            float s = S[sb][r] * cs;
-            if (HAS_GS) s += g_i - Gj[kk];
-            if (masked) {
-              const int64_t j = kj0 + kk;
-              if (j > qi || (window > 0 && qi - j >= window)) s = -INFINITY;
-            }
-            S[sb][r] = s;
-          }
-        }
-        cs = 1.f;
-      }
-      float mx = -INFINITY;
+    }
+    float cs = csig_cur;
+    if (HAS_GS) {
+      // the row term Gs[i] is constant along the softmax row; it is restored
+      // for the sink and lse in the epilogue
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * cs;
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
+        for (int j = 0; j < 4; ++j) {
+          const float4 gj = *reinterpret_cast<const float4 *>(&Gj[buf][sb * 32 + 8 * j + 4 * half]);
+          S[sb][4 * j + 0] = fmaf(S[sb][4 * j + 0], cs, -gj.x);
+          S[sb][4 * j + 1] = fmaf(S[sb][4 * j + 1], cs, -gj.y);
+          S[sb][4 * j + 2] = fmaf(S[sb][4 * j + 2], cs, -gj.z);
+          S[sb][4 * j + 3] = fmaf(S[sb][4 * j + 3], cs, -gj.w);
+        }
+      cs = 1.f;
+    }
+    const bool masked = (kj0 + BN - 1 > qw0) || (window > 0 && qw0 + WROWS - 1 - kj0 >= window);
+    if (masked) {
+      const int rel = rel0 - kj0;  // key offsets kk (without the 4*half part) allowed: kk <= rel
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(S[sb][r], cs, -m_use));
-          S[sb][r] = p;
-          rs += p;
+          const int kk = sb * 32 + 8 * (r >> 2) + (r & 3);
+          bool ok = kk <= rel;
+          if (window > 0) ok = ok && (rel - kk < window);
+          S[sb][r] = ok ? S[sb][r] : -INFINITY;
         }
-      rs += __shfl_xor(rs, 32);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * cs;
+    const bool raise = mx > m_run + TAU;  // also true on the first visible tile
+    if (__ballot(raise)) {
+      // lanes that keep their max scale by exactly 1 (their max may still be
+      // -inf if no key has been visible to them yet)
+      const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
+      l_run *= alpha;
 #pragma unroll
       for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] *= alpha;
-      bf16x8 pB[4];
+      m_run = raise ? mx : m_run;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float rs = 0.f;
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
+    for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pB[s][e] = (__bf16)S[s >> 1][8 * (s & 1) + e];
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(S[sb][r], cs, -m_use));
+        S[sb][r] = p;
+        rs += p;
+      }
+    rs += __shfl_xor(rs, 32);
+    l_run += rs;
+    bf16x8 pB[4];
 #pragma unroll
-      for (int mb = 0; mb < DV / 32; ++mb) {
+    for (int s = 0; s < 4; ++s) {
+      const f32x16 &src = S[s >> 1];
+      const f32x8 p8 = (s & 1) ? __builtin_shufflevector(src, src, 8, 9, 10, 11, 12, 13, 14, 15)
+                               : __builtin_shufflevector(src, src, 0, 1, 2, 3, 4, 5, 6, 7);
+      pB[s] = __builtin_convertvector(p8, bf16x8);
+    }
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const bf16x8 a =
-              *reinterpret_cast<const bf16x8 *>(&Vt[(mb * 32 + col) * VS + s * 16 + half * 8]);
-          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[s], oacc[mb], 0, 0, 0);
-        }
+    for (int mb = 0; mb < DV / 32; ++mb) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8 *>(&Vt[buf][(mb * 32 + col) * VS + s * 16 + half * 8]);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[s], oacc[mb], 0, 0, 0);
       }
     }
-    __syncthreads();
-    if (J < Jhi) store_tile();
-    csig = csig_next;
   }
 
   if (!q_ok) return;
+  // scores above are relative to the row term Gs[i] (g_i); restore it here
   float mf = m_run, Z = l_run;
   if (sink != nullptr) {
-    const float s2 = sink[hq] * LOG2E;
+    const float s2 = sink[hq] * LOG2E - g_i;
     mf = fmaxf(m_run, s2);
     Z = l_run * fast_exp2(m_run - mf) + fast_exp2(s2 - mf);
   }
   const float inv = fast_exp2(m_run - mf) / Z;
-  bf16_t *orow = o + (qi * HQ + hq) * DV;
+  bf16_t *orow = o + ((bos64 + qi) * HQ + hq) * DV;
 #pragma unroll
   for (int mb = 0; mb < DV / 32; ++mb)
 #pragma unroll
@@ -292,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
       w.y = pack_bf16x2(oacc[mb][4 * j + 2] * inv, oacc[mb][4 * j + 3] * inv);
       *reinterpret_cast<u32x2 *>(orow + mb * 32 + 8 * j + 4 * half) = w;
     }
-  if (lse != nullptr && half == 0) lse[qi * HQ + hq] = (mf + log2f(Z)) * LN2;
+  if (lse != nullptr && half == 0) lse[(bos64 + qi) * HQ + hq] = (mf + g_i + log2f(Z)) * LN2;
 }
 
 // fp32 kernel: plain FMA arithmetic, one 64-row chunk of queries per
@@ -414,7 +453,8 @@ hipError_t attn_bf16_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t 
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const _Float16 *>(ws.qh),
                        static_cast<const _Float16 *>(ws.kt), static_cast<const bf16_t *>(p.v),
                        ws.anch, ws.gsum, p.sink, static_cast<bf16_t *>(p.o), p.lse, p.cu, p.T,
-                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT, p.window);
+                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT,
+                       (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0));
   };
   if (p.g_scalar != nullptr)
     args(k_attn_fwd_bf16<DK, DV, true>);

@@ -99,8 +99,10 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
 }
 
 // Phase B: exclusive scan of the chunk sums along time (in place), and the
-// chunk anchors anch[c] = (offset + sum of chunk c) * log2(e) = P2 at the
-// chunk's last token.  Channel index KD stands for g_scalar.
+// chunk anchors anch[c] = the integer nearest to P2 at the chunk's last token,
+// (offset + sum of chunk c) * log2(e).  Any anchor cancels in the score; an
+// integer one makes every tile-pair factor 2^(RQ_I - R_J) an exact power of
+// two, applied without rounding.  Channel index KD stands for g_scalar.
 // grid (HQ, nseg, ceil((KD+1)/32)), 256 threads = 32 channels x 8 chunk groups.
 template <int KD>
 __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
   for (int c = cb; c < ce; ++c) {
     const float x = p[c * stride];
     p[c * stride] = run;
-    if (ch < KD) a[c * stride] = (run + x) * LOG2E;
+    if (ch < KD) a[c * stride] = rintf((run + x) * LOG2E);
     run += x;
   }
 }
