@@ -42,6 +42,26 @@ namespace {
 constexpr int BN = CHUNK;  // keys per tile
 constexpr int WROWS = 32;  // query rows per wave
 
+// Bounds-checked 16-byte load through a buffer resource: offsets past the
+// resource's extent read as zero, and the per-tile offset is a scalar.
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0,
+                                           (int)min<int64_t>(bytes, 0x7fffffff), 0x00020000);
+}
+// Values of lanes l and l^32 combined: v_permlane32_swap exchanges the two
+// half-waves without going through LDS.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int DK, int DV, bool HAS_GS>
 __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
     const _Float16 *__restrict__ qh, const _Float16 *__restrict__ kt, const bf16_t *__restrict__ v,
@@ -49,12 +69,18 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
     const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int nseg, int NCmax, int NQT,
     int window) {
-  constexpr int KS = DK + 8;  // LDS row stride (elements) of the key tile
-  constexpr int VS = BN + 8;  // LDS row stride (elements) of the transposed value tile
-  // double-buffered tiles: one barrier per key tile
+  // Key tile rows hold DK decayed channels plus one extra 16-channel block
+  // that folds the softmax shift and the gate into the same MFMA:
+  //   extra channels of key j:   [2^-s, 2^-s, -Gs_j hi * 2^-s, -Gs_j lo * 2^-s, 0 ...]
+  //   extra channels of query i: [-m_i hi, -m_i lo, 1, 1, 0 ...]
+  // so the MFMA returns (score - running max) / 2^s directly (s = sigma of
+  // the tile, almost always 0) and the common path needs only the exp2.
+  constexpr int KX = DK + 16;      // channels per staged key row
+  constexpr int KS = KX + 8;       // LDS row stride (elements) of the key tile
+  constexpr int VS = BN + 8;       // LDS row stride (elements) of the transposed value tile
+  constexpr int NKS = KX / 16;     // MFMA k-steps of the score product
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KS];  // half bits
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DV * VS];
-  __shared__ __attribute__((aligned(16))) float Gj[2][BN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hq = blockIdx.x % HQ;
@@ -81,103 +107,121 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
   const int qi = qw0 + col;
   const bool q_ok = qi < L;
 
-  // per-head bases (token strides: HQ*DK for q_hat/k_tilde, H*DV for v)
-  const _Float16 *qh_b = qh + (bos64 * HQ + hq) * DK;
-  const _Float16 *kt_b = kt + (bos64 * HQ + hq) * DK;
-  const bf16_t *v_b = v + (bos64 * H + h) * DV;
-  const float *gs_b = HAS_GS ? gsum + bos64 * HQ + hq : nullptr;
+  // per-sequence, per-head buffer resources (byte offsets; rows past L read 0)
   const int qrow = HQ * DK, vrow = H * DV;
+  const __amdgpu_buffer_rsrc_t kt_rs = make_rsrc(kt + (bos64 * HQ + hq) * DK, (int64_t)L * qrow * 2);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + (bos64 * H + h) * DV, (int64_t)L * vrow * 2);
+  const float *gs_b = HAS_GS ? gsum + bos64 * HQ + hq : nullptr;
 
-  f16x8 qB[DK / 16];
-#pragma unroll
-  for (int ks = 0; ks < DK / 16; ++ks) {
+  f16x8 qB[NKS];
+  {
+    const _Float16 *qh_b = qh + (bos64 * HQ + hq) * DK;
     const int r = q_ok ? qi : L - 1;
-    qB[ks] = *reinterpret_cast<const f16x8 *>(qh_b + r * qrow + ks * 16 + half * 8);
+#pragma unroll
+    for (int ks = 0; ks < DK / 16; ++ks)
+      qB[ks] = *reinterpret_cast<const f16x8 *>(qh_b + r * qrow + ks * 16 + half * 8);
   }
   const float g_i = (HAS_GS && q_ok) ? gs_b[qi * HQ] : 0.f;
+  // running max of (score - Gs_i) in log2 units; 0 until the first visible key
+  float m_run = 0.f;
+  bool m_unset = true;
+  auto set_qx = [&]() {
+    const _Float16 mh = (_Float16)(-m_run);
+    const _Float16 ml = (_Float16)(-m_run - (float)mh);
+    f16x8 x = f16x8{};
+    if (half == 0) {
+      x[0] = mh;
+      x[1] = ml;
+      x[2] = (_Float16)1.f;
+      x[3] = (_Float16)1.f;
+    }
+    qB[NKS - 1] = x;
+  };
+  set_qx();
 
   // staging roles
   constexpr int KCP = DK / 8;      // 16-byte pieces per key row
   constexpr int KRP = 256 / KCP;   // key rows per pass
   constexpr int KNP = BN / KRP;    // passes
   const int cp = tid % KCP, kr = tid / KCP;
+  const int koff = (kr * qrow + cp * 8) * 2;  // byte offset of this thread's first piece
   constexpr int VNB = (DV / 8) * 16;  // 4-key x 8-channel blocks of the value tile
   const int kq = tid % 16, cg = tid / 16;
   const bool v_role = tid < VNB;
+  const int voff = (4 * kq * vrow + cg * 8) * 2;
   const int sq = kq & 3;
   const int vpos = 16 * (kq >> 2) + 4 * (sq >> 1) + 8 * (sq & 1);
 
   const int64_t cbase = (int64_t)seg * NCmax;
   const int cq = 2 * I;  // the query tile's anchor: its first chunk
-  float RQ[8];
-  {
-    const float *ap = anch + ((cbase + cq) * HQ + hq) * DK + cp * 8;
-    const float4 a0 = *reinterpret_cast<const float4 *>(ap);
-    const float4 a1 = *reinterpret_cast<const float4 *>(ap + 4);
-    RQ[0] = a0.x; RQ[1] = a0.y; RQ[2] = a0.z; RQ[3] = a0.w;
-    RQ[4] = a1.x; RQ[5] = a1.y; RQ[6] = a1.z; RQ[7] = a1.w;
-  }
+
+  // Tile-pair decay factors d_IJ = 2^(RQ_I - R_J): the prefill anchors are
+  // integers, so the exponents are exact integers and the factors exact powers
+  // of two.  Wave 0 computes them for the tile two steps ahead (lane l: the
+  // channel pair 2l, 2l+1) and publishes packed half pairs in LDS together
+  // with 2^sigma; sigma > 0 only if some factor exceeds 2^8 (the decay sum
+  // rose between key tile and query tile), and then the staged operand is
+  // scaled by 2^-sigma and the scores by 2^sigma.
+  __shared__ __attribute__((aligned(16))) uint32_t Dsh[2][DK / 2];
+  __shared__ float Csh[2];
+  constexpr int DPAIRS = DK / 2;
+  const int dl = lane % DPAIRS;  // wave 0: channel pair of this lane
+  float2 rq2 = make_float2(0.f, 0.f), an2 = make_float2(0.f, 0.f);
+  const float *anch_b = anch + (cbase * HQ + hq) * DK + 2 * dl;
+  if (wave == 0) rq2 = *reinterpret_cast<const float2 *>(anch_b + (int64_t)cq * HQ * DK);
+  auto publish_d = [&](int slot) {  // wave 0 only
+    const float e0 = rq2.x - an2.x, e1 = rq2.y - an2.y;
+    const float emax = wave_max(fmaxf(e0, e1));
+    const int sigma = emax > 8.f ? (int)emax - 8 : 0;
+    const int x0 = max((int)e0 - sigma, -30), x1 = max((int)e1 - sigma, -30);
+    const uint32_t w = pack_f16x2(__builtin_amdgcn_ldexpf(1.f, x0), __builtin_amdgcn_ldexpf(1.f, x1));
+    if (lane < DPAIRS) Dsh[slot][lane] = w;
+    if (lane == 0) Csh[slot] = __builtin_amdgcn_ldexpf(1.f, sigma);
+  };
 
   u32x4 kreg[KNP];
   u32x4 vreg[4];
-  uint32_t dpk[4];       // per-channel-pair decay factors, exact powers of two in half
-  float csig_next = 1.f;  // 2^sigma of the tile held in registers
   float gj_reg = 0.f;
 
   auto load_tile = [&](int J) {
     const int kj0 = J * BN;
-    const bool full = kj0 + BN <= L;
-    const _Float16 *kb = kt_b + kj0 * qrow;
 #pragma unroll
-    for (int p = 0; p < KNP; ++p) {
-      int r = kr + p * KRP;
-      if (!full) r = min(r, L - 1 - kj0);  // rows past the end are masked; keep reads in bounds
-      kreg[p] = *reinterpret_cast<const u32x4 *>(kb + r * qrow + cp * 8);
-    }
+    for (int p = 0; p < KNP; ++p) kreg[p] = buf_load16(kt_rs, koff + p * KRP * qrow * 2, kj0 * qrow * 2);
     if (v_role) {
-      const bf16_t *vb = v_b + kj0 * vrow + cg * 8;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int rr = 4 * kq + r;
-        if (!full) rr = min(rr, L - 1 - kj0);
-        vreg[r] = *reinterpret_cast<const u32x4 *>(vb + rr * vrow);
-      }
+      for (int r = 0; r < 4; ++r) vreg[r] = buf_load16(v_rs, voff + r * vrow * 2, kj0 * vrow * 2);
     }
     if (HAS_GS && tid < BN) gj_reg = gs_b[min(kj0 + tid, L - 1) * HQ];
-    // d_IJ = 2^(RQ - R_J): the prefill anchors are integers, so the exponents
-    // are exact integers and the factors exact powers of two
-    const float *ap = anch + ((cbase + J) * HQ + hq) * DK + cp * 8;
-    const float4 a0 = *reinterpret_cast<const float4 *>(ap);
-    const float4 a1 = *reinterpret_cast<const float4 *>(ap + 4);
-    float e[8] = {RQ[0] - a0.x, RQ[1] - a0.y, RQ[2] - a0.z, RQ[3] - a0.w,
-                  RQ[4] - a1.x, RQ[5] - a1.y, RQ[6] - a1.z, RQ[7] - a1.w};
-    float emax = fmaxf(fmaxf(fmaxf(e[0], e[1]), fmaxf(e[2], e[3])),
-                       fmaxf(fmaxf(e[4], e[5]), fmaxf(e[6], e[7])));
-#pragma unroll
-    for (int o2 = 1; o2 < KCP; o2 <<= 1) emax = fmaxf(emax, __shfl_xor(emax, o2));
-    // keep the staged half operands below 2^8 * |k_tilde|; scores are scaled back by 2^sigma
-    const int sigma = emax > 8.f ? (int)emax - 8 : 0;
-    csig_next = __builtin_amdgcn_ldexpf(1.f, sigma);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int e0 = max((int)e[2 * w] - sigma, -30), e1 = max((int)e[2 * w + 1] - sigma, -30);
-      dpk[w] = pack_f16x2(__builtin_amdgcn_ldexpf(1.f, e0), __builtin_amdgcn_ldexpf(1.f, e1));
-    }
+    if (wave == 0) an2 = *reinterpret_cast<const float2 *>(anch_b + (int64_t)J * HQ * DK);
   };
 
   auto store_tile = [&](int buf) {
+    const u32x4 dpk = *reinterpret_cast<const u32x4 *>(&Dsh[buf][cp * 4]);
+    const float csg = Csh[buf];
 #pragma unroll
     for (int p = 0; p < KNP; ++p) {
       u32x4 out;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        // copy the vector element to a scalar first: bit-casting the element
+        // copy the vector elements to scalars first: bit-casting an element
         // expression directly has been seen to read element 0
         const uint32_t kw = kreg[p][w], dw = dpk[w];
         const f16x2 prod = __builtin_bit_cast(f16x2, kw) * __builtin_bit_cast(f16x2, dw);
         out[w] = __builtin_bit_cast(uint32_t, prod);
       }
       *reinterpret_cast<u32x4 *>(&Ks[buf][(kr + p * KRP) * KS + cp * 8]) = out;
+    }
+    if (tid < BN) {  // the extra channels of key row tid
+      const float inv = 1.f / csg;  // exact: a power of two
+      u32x4 x = u32x4{0, 0, 0, 0};
+      x[0] = pack_f16x2(inv, inv);
+      if (HAS_GS) {
+        const float gsc = -gj_reg * inv;
+        const _Float16 gh = (_Float16)gsc;
+        x[1] = pack_f16x2((float)gh, gsc - (float)gh);
+      }
+      *reinterpret_cast<u32x4 *>(&Ks[buf][tid * KS + DK]) = x;
+      *reinterpret_cast<u32x4 *>(&Ks[buf][tid * KS + DK + 8]) = u32x4{0, 0, 0, 0};
     }
     if (v_role) {
 #pragma unroll
@@ -194,122 +238,122 @@ __global__ __launch_bounds__(256, 2) void k_attn_fwd_bf16(
         *reinterpret_cast<u32x2 *>(&Vt[buf][(cg * 8 + c) * VS + vpos]) = out;
       }
     }
-    if (HAS_GS && tid < BN) Gj[buf][tid] = gj_reg;
+    return csg;
   };
 
-  // Online softmax state of this lane's query (log2 units).  The running max
-  // is raised only when a tile's max exceeds it by more than 2^8 (exp2 of the
-  // scores stays below 256, far inside fp32 and bf16 range), so the output
-  // accumulators are rescaled rarely.
+  // Online softmax.  The running max is raised only when a tile's max exceeds
+  // it by more than 2^8 (exp2 of the shifted scores stays below 256, far
+  // inside fp32 and bf16 range), so the output accumulators and the query's
+  // shift channels change rarely.
   constexpr float TAU = 8.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float l_run = 0.f;
   f32x16 oacc[DV / 32];
 #pragma unroll
   for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] = f32x16{};
 
+  // Pipeline: tile J computes from LDS buffer J&1 while tile J+1 is staged
+  // into the other buffer and tile J+2 is being loaded into registers.  The
+  // schedule is unconditional (tiles past Jhi repeat Jhi; their buffers are
+  // never read) so registers need no copies between iterations.
   load_tile(Jlo);
-  store_tile(Jlo & 1);
-  float csig_cur = csig_next;  // 2^sigma of the tile being computed
-  float csig_stg = 1.f;        // 2^sigma of the tile staged in the other buffer
-  if (Jlo < Jhi) load_tile(Jlo + 1);
+  if (wave == 0) publish_d(Jlo & 1);
+  __syncthreads();
+  float csig_cur = store_tile(Jlo & 1);
+  load_tile(min(Jlo + 1, Jhi));
+  if (wave == 0) publish_d((Jlo + 1) & 1);
   const int rel0 = qi - 4 * half;  // query position minus this lane's key sub-offset
 
-  for (int J = Jlo; J <= Jhi; ++J, csig_cur = csig_stg) {
+  for (int J = Jlo; J <= Jhi; ++J) {
     const int buf = J & 1;
     __syncthreads();  // tile J is in LDS; every wave has finished reading the other buffer
-    if (J < Jhi) {
-      store_tile(buf ^ 1);
-      csig_stg = csig_next;
-      if (J + 1 < Jhi) load_tile(J + 2);
-    }
+    const float csig_stg = store_tile(buf ^ 1);
+    load_tile(min(J + 2, Jhi));
     const int kj0 = J * BN;
     const bool need = wave_live && kj0 <= qw_last && kj0 + BN - 1 >= jw_lo;
-    if (!need) continue;
-    f32x16 S[2];
+    if (need) {
+      f32x16 S[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      S[sb] = f32x16{};
+      for (int sb = 0; sb < 2; ++sb) {
+        S[sb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks) {
-        const f16x8 a =
-            *reinterpret_cast<const f16x8 *>(&Ks[buf][(sb * 32 + col) * KS + ks * 16 + half * 8]);
-        S[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[ks], S[sb], 0, 0, 0);
+        for (int ks = 0; ks < NKS; ++ks) {
+          const f16x8 a =
+              *reinterpret_cast<const f16x8 *>(&Ks[buf][(sb * 32 + col) * KS + ks * 16 + half * 8]);
+          S[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[ks], S[sb], 0, 0, 0);
+        }
       }
-    }
-    float cs = csig_cur;
-    if (HAS_GS) {
-      // the row term Gs[i] is constant along the softmax row; it is restored
-      // for the sink and lse in the epilogue
+      const float cs = csig_cur;  // scores are S * cs
+      const bool masked = (kj0 + BN - 1 > qw0) || (window > 0 && qw0 + WROWS - 1 - kj0 >= window);
+      if (masked) {
+        const int rel = rel0 - kj0;  // allowed key offsets kk (without the 4*half part): kk <= rel
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = sb * 32 + 8 * (r >> 2) + (r & 3);
+            bool ok = kk <= rel;
+            if (window > 0) ok = ok && (rel - kk < window);
+            S[sb][r] = ok ? S[sb][r] : -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float4 gj = *reinterpret_cast<const float4 *>(&Gj[buf][sb * 32 + 8 * j + 4 * half]);
-          S[sb][4 * j + 0] = fmaf(S[sb][4 * j + 0], cs, -gj.x);
-          S[sb][4 * j + 1] = fmaf(S[sb][4 * j + 1], cs, -gj.y);
-          S[sb][4 * j + 2] = fmaf(S[sb][4 * j + 2], cs, -gj.z);
-          S[sb][4 * j + 3] = fmaf(S[sb][4 * j + 3], cs, -gj.w);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sb][r]);
+      mx = half_max(mx) * cs;  // tile max minus the running max
+      const bool raise = m_unset ? mx > -INFINITY : mx > TAU;
+      const bool any_raise = __ballot(raise) != 0;
+      if (any_raise || cs != 1.f) {
+        // rare: a lane raises its max, or the tile was staged with 2^-sigma
+        __asm__ volatile("s_nop 0");  // keep this a branch
+        const float shift = raise ? mx : 0.f;
+        if (any_raise) {
+          // lanes that keep their max scale by exactly 1; a lane's first
+          // visible tile has nothing accumulated yet
+          const float alpha = raise ? (m_unset ? 0.f : fast_exp2(-mx)) : 1.f;
+          l_run *= alpha;
+#pragma unroll
+          for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] *= alpha;
+          m_run += shift;
+          m_unset = m_unset && !raise;
+          set_qx();
         }
-      cs = 1.f;
-    }
-    const bool masked = (kj0 + BN - 1 > qw0) || (window > 0 && qw0 + WROWS - 1 - kj0 >= window);
-    if (masked) {
-      const int rel = rel0 - kj0;  // key offsets kk (without the 4*half part) allowed: kk <= rel
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) S[sb][r] = fmaf(S[sb][r], cs, -shift);
+      }
+      float rs = 0.f;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int kk = sb * 32 + 8 * (r >> 2) + (r & 3);
-          bool ok = kk <= rel;
-          if (window > 0) ok = ok && (rel - kk < window);
-          S[sb][r] = ok ? S[sb][r] : -INFINITY;
+          const float p = fast_exp2(S[sb][r]);
+          S[sb][r] = p;
+          rs += p;
         }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[sb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * cs;
-    const bool raise = mx > m_run + TAU;  // also true on the first visible tile
-    if (__ballot(raise)) {
-      // lanes that keep their max scale by exactly 1 (their max may still be
-      // -inf if no key has been visible to them yet)
-      const float alpha = raise ? fast_exp2(m_run - mx) : 1.f;
-      l_run *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < DV / 32; ++mb) oacc[mb] *= alpha;
-      m_run = raise ? mx : m_run;
-    }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(S[sb][r], cs, -m_use));
-        S[sb][r] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 32);
-    l_run += rs;
-    bf16x8 pB[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f32x16 &src = S[s >> 1];
-      const f32x8 p8 = (s & 1) ? __builtin_shufflevector(src, src, 8, 9, 10, 11, 12, 13, 14, 15)
-                               : __builtin_shufflevector(src, src, 0, 1, 2, 3, 4, 5, 6, 7);
-      pB[s] = __builtin_convertvector(p8, bf16x8);
-    }
-#pragma unroll
-    for (int mb = 0; mb < DV / 32; ++mb) {
+      l_run += half_sum(rs);
+      bf16x8 pB[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8 *>(&Vt[buf][(mb * 32 + col) * VS + s * 16 + half * 8]);
-        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[s], oacc[mb], 0, 0, 0);
+        const f32x16 &src = S[s >> 1];
+        const f32x8 p8 = (s & 1) ? __builtin_shufflevector(src, src, 8, 9, 10, 11, 12, 13, 14, 15)
+                                 : __builtin_shufflevector(src, src, 0, 1, 2, 3, 4, 5, 6, 7);
+        pB[s] = __builtin_convertvector(p8, bf16x8);
+      }
+#pragma unroll
+      for (int mb = 0; mb < DV / 32; ++mb) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8 *>(&Vt[buf][(mb * 32 + col) * VS + s * 16 + half * 8]);
+          oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[s], oacc[mb], 0, 0, 0);
+        }
       }
     }
+    if (wave == 0) publish_d(buf);  // factors of tile min(J+2, Jhi), staged next iteration
+    csig_cur = csig_stg;
   }
 
   if (!q_ok) return;
