@@ -55,8 +55,13 @@ struct Vec8<float> {
 
 // grid (nsplit, HQ/NHB, B), 256 threads.  The cache holds k_tilde in the
 // operand type TK (IEEE half for bf16 inputs).
+//
+// Memory-level parallelism: every 16-byte piece of the next chunk's keys and
+// values is requested as soon as the same piece of the current chunk has been
+// consumed, so one register set holds both the data in use and the data in
+// flight (about one chunk ahead) and the kernel runs three workgroups per CU.
 template <typename TE, int DK, int DV, int NHB, typename TK = typename OperandOf<TE>::type>
-__global__ __launch_bounds__(256) void k_decode_split(
+__global__ __launch_bounds__(256, 3) void k_decode_split(
     const TE *__restrict__ q, const TE *__restrict__ v, const float *__restrict__ p_curr,
     const TK *__restrict__ kt, const float *__restrict__ rc, float *__restrict__ part_o,
     float *__restrict__ part_ml, int64_t T, int HQ, int H, int NC, int nsplit, int cps,
@@ -69,8 +74,8 @@ __global__ __launch_bounds__(256) void k_decode_split(
   constexpr int QN = NHB * DK;        // rescaled query values per chunk
   constexpr int QPT = (QN + 255) / 256;
 
-  __shared__ float Qs[2][NHB][DK];
-  __shared__ float Ps[2][C][NHB];
+  __shared__ __attribute__((aligned(16))) float Qs[2][NHB][DK];
+  __shared__ __attribute__((aligned(16))) float Ps[2][C][NHB];
   __shared__ float Al[2][NHB];
   __shared__ float red[KL][NHB][DV];
 
@@ -98,35 +103,25 @@ __global__ __launch_bounds__(256) void k_decode_split(
     }
   };
 
-  // score role: head sh = wave, key kk = lane
+  // score role: head sh = wave, key kk = lane.  Keys past T_kv are read at
+  // the last key (in bounds) and masked.
   const int sh = wave, kk = lane;
   const bool s_role = sh < NHB;
-  Vec8<TK> kreg[KV8];
-  auto load_k = [&](int c) {
-    const int64_t j = (int64_t)c * C + kk;
-    if (s_role && j < T) {
-      const TK *kp = kt + ((tb + j) * HQ + hq0 + sh) * DK;
-#pragma unroll
-      for (int i = 0; i < KV8; ++i) kreg[i].load(kp + 8 * i);
-    } else {
-#pragma unroll
-      for (int i = 0; i < KV8; ++i) kreg[i].zero();
-    }
+  const TK *kt_row = kt + (tb * HQ + hq0 + (s_role ? sh : 0)) * DK;
+  auto kptr = [&](int c) {
+    const int64_t j = min((int64_t)c * C + kk, T - 1);
+    return kt_row + j * HQ * DK;
   };
+  Vec8<TK> kreg[KV8];
 
   // PV role: channel group cg, key lane kl
   const int cg = tid % VCG, kl = tid / VCG;
-  Vec8<TE> vreg[KPL];
-  auto load_v = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-      const int64_t j = (int64_t)c * C + kl + KL * i;
-      if (j < T)
-        vreg[i].load(v + ((tb + j) * H + h) * DV + cg * 8);
-      else
-        vreg[i].zero();
-    }
+  const TE *v_row = v + (tb * H + h) * DV + cg * 8;
+  auto vptr = [&](int c, int i) {
+    const int64_t j = min((int64_t)c * C + kl + KL * i, T - 1);
+    return v_row + j * H * DV;
   };
+  Vec8<TE> vreg[KPL];
 
   float m_run = -INFINITY, l_run = 0.f;  // per score wave (its head)
   float oacc[NHB][8];
@@ -136,26 +131,42 @@ __global__ __launch_bounds__(256) void k_decode_split(
     for (int e = 0; e < 8; ++e) oacc[hh][e] = 0.f;
 
   load_r(c_begin);
-  load_k(c_begin);
-  load_v(c_begin);
+  if (s_role) {
+    const TK *kp = kptr(c_begin);
+#pragma unroll
+    for (int i = 0; i < KV8; ++i) kreg[i].load(kp + 8 * i);
+  }
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) vreg[i].load(vptr(c_begin, i));
+
   for (int c = c_begin; c < c_end; ++c) {
     const int buf = c & 1;
-    const bool more = c + 1 < c_end;
+    const int cn = min(c + 1, c_end - 1);  // next chunk (the last one repeats)
 #pragma unroll
     for (int i = 0; i < QPT; ++i) {
       const int x = tid + 256 * i;
       if (x < QN) Qs[buf][x / DK][x % DK] = qreg[i] * fast_exp2(preg[i] - rreg[i]) * qscale;
     }
-    if (more) load_r(c + 1);
+    load_r(cn);
     __syncthreads();
     if (s_role) {
+      const TK *kp = kptr(cn);
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < KV8; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(Qs[buf][sh][8 * i + e], kreg[i][e], s);
+      for (int i = 0; i < KV8; ++i) {
+        const float4 qa = *reinterpret_cast<const float4 *>(&Qs[buf][sh][8 * i]);
+        const float4 qb = *reinterpret_cast<const float4 *>(&Qs[buf][sh][8 * i + 4]);
+        s = fmaf(qa.x, kreg[i][0], s);
+        s = fmaf(qa.y, kreg[i][1], s);
+        s = fmaf(qa.z, kreg[i][2], s);
+        s = fmaf(qa.w, kreg[i][3], s);
+        s = fmaf(qb.x, kreg[i][4], s);
+        s = fmaf(qb.y, kreg[i][5], s);
+        s = fmaf(qb.z, kreg[i][6], s);
+        s = fmaf(qb.w, kreg[i][7], s);
+        kreg[i].load(kp + 8 * i);  // same piece of the next chunk
+      }
       if ((int64_t)c * C + kk >= T) s = -INFINITY;
-      if (more) load_k(c + 1);
       const float cm = wave_max(s);
       const float m_new = fmaxf(m_run, cm);  // finite: every chunk has a valid key
       const float p = fast_exp2(s - m_new);
@@ -177,16 +188,21 @@ __global__ __launch_bounds__(256) void k_decode_split(
     for (int i = 0; i < KPL; ++i) {
       const int key = kl + KL * i;
       float pp[NHB];
+      if (NHB == 4) {
+        const float4 p4 = *reinterpret_cast<const float4 *>(&Ps[buf][key][0]);
+        pp[0] = p4.x; pp[1 % NHB] = p4.y; pp[2 % NHB] = p4.z; pp[3 % NHB] = p4.w;
+      } else {
 #pragma unroll
-      for (int hh = 0; hh < NHB; ++hh) pp[hh] = Ps[buf][key][hh];
+        for (int hh = 0; hh < NHB; ++hh) pp[hh] = Ps[buf][key][hh];
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float ve = vreg[i][e];
 #pragma unroll
         for (int hh = 0; hh < NHB; ++hh) oacc[hh][e] = fmaf(pp[hh], ve, oacc[hh][e]);
       }
+      vreg[i].load(vptr(cn, i));  // same piece of the next chunk
     }
-    if (more) load_v(c + 1);
   }
 
   // reduce partial outputs across key lanes
@@ -283,7 +299,7 @@ void decode_split_plan(int64_t B, int64_t T, int64_t HQ, int64_t H, int *nsplit,
                        int *chunks_per_split) {
   const int64_t NC = (T + CHUNK - 1) / CHUNK;
   const int64_t units = B * (HQ / heads_per_block(HQ, H));
-  const int64_t target = 8192;  // workgroups: 32 per CU on 256 CUs
+  const int64_t target = 256 * 3 * 8;  // eight full waves of 3 resident workgroups per CU
   int64_t ns = (target + units - 1) / units;
   ns = ns < 1 ? 1 : (ns > NC ? NC : ns);
   const int64_t cps = (NC + ns - 1) / ns;
