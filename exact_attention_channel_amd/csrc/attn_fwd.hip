@@ -48,8 +48,10 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff,
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
 }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0,
-                                           (int)min<int64_t>(bytes, 0x7fffffff), 0x00020000);
+  // integer select: HIP's min() on 64-bit integers goes through f64 VALU code,
+  // which would make the descriptor a vector value (and each load a loop)
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, 0x00020000);
 }
 // Values of lanes l and l^32 combined: v_permlane32_swap exchanges the two
 // half-waves without going through LDS.

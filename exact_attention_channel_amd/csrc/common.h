@@ -81,8 +81,16 @@ template <typename TE> struct OperandOf;
 template <> struct OperandOf<bf16_t> { typedef _Float16 type; };
 template <> struct OperandOf<float> { typedef float type; };
 
+// A workgroup-uniform value moved into scalar registers, so that everything
+// derived from it (addresses, buffer descriptors, loop bounds) stays scalar.
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Token range [bos, eos) of segment s: batch row s of length T, or the packed
-// sequence s of cu_seqlens.
+// sequence s of cu_seqlens.  s must be uniform across the workgroup.
 __device__ __forceinline__ void segment_bounds(int s, int64_t T, const int32_t *cu, int64_t &bos,
                                                int64_t &eos) {
   if (cu) {
@@ -92,6 +100,8 @@ __device__ __forceinline__ void segment_bounds(int s, int64_t T, const int32_t *
     bos = (int64_t)s * T;
     eos = bos + T;
   }
+  bos = uniform64(bos);
+  eos = uniform64(eos);
 }
 
 __device__ __forceinline__ float wave_max(float x) {
