@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
   segment_bounds(s, T, cu, bos, eos);
   const int64_t r0 = bos + (int64_t)c * CHUNK;
   if (r0 >= eos) return;
-  const int nrow = (int)min<int64_t>(CHUNK, eos - r0);
+  const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
   constexpr int NG = 256 / KD;
   const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
   float acc = 0.f;
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   segment_bounds(s, T, cu, bos, eos);
   const int64_t r0 = bos + (int64_t)c * CHUNK;
   if (r0 >= eos) return;
-  const int nrow = (int)min<int64_t>(CHUNK, eos - r0);
+  const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
   const int h = hq / (HQ / H);
   constexpr int NG = 256 / KD;
   constexpr int RPG = CHUNK / NG;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
   segment_bounds(s, T, cu, bos, eos);
   const int64_t r0 = bos + (int64_t)c * CHUNK;
   if (r0 >= eos) return;
-  const int nrow = (int)min<int64_t>(CHUNK, eos - r0);
+  const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
   constexpr int NG = 256 / KD;
   constexpr int RPG = CHUNK / NG;
   const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
@@ -256,7 +256,7 @@ __global__ __launch_bounds__(256) void k_build_cache(const TE *__restrict__ k,
                                                      int64_t T, int HQ, int H, int NC) {
   const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
   const int64_t r0 = (int64_t)c * CHUNK;
-  const int nrow = (int)min<int64_t>(CHUNK, T - r0);
+  const int nrow = (T - r0) < CHUNK ? (int)(T - r0) : CHUNK;
   const int h = hq / (HQ / H);
   constexpr int NQ = KD / 4;
   constexpr int NRG = 256 / NQ;

@@ -135,6 +135,30 @@ def test_config_usage_bf16_g_zero_is_softmax_attention(wa):
     check(o, sd, 2e-2, c.name + " vs SDPA")
 
 
+REF_OVERFLOW = [
+    cfg("bf16_T700_D128_rising_gate", 1, 700, 4, 2, 128, 128, torch.bfloat16, g_mode="neg_softplus",
+        g_std=0.05, sink=True, seed=21),
+    cfg("bf16_varlen_window150_K64_rising_gate", 1, 0, 4, 2, 64, 64, torch.bfloat16, nseq=5,
+        len_lo=40, len_hi=500, window=150, seed=22),
+]
+
+
+@pytest.mark.parametrize("c", REF_OVERFLOW, ids=[c.name for c in REF_OVERFLOW])
+def test_prefill_gate_favouring_old_keys(wa, c):
+    """A positive g_scalar (the running gate sum grows along the sequence) puts
+    the largest scores on the oldest visible keys, hundreds of log2 units above
+    the newest ones: the kernel's per-row reference taken from the newest keys
+    cannot hold those probabilities, and the recompute with the exact row max
+    must give the oracle's result."""
+    x = W.make_prefill(c)
+    shape = x["q"].shape[:3]
+    x["g_scalar"] = torch.full(shape, 0.5, dtype=c.dtype)
+    o, lse = run_gpu(wa, x)
+    ro, rl = run_oracle(x)
+    check(o, ro, TOL[c.dtype], c.name + " o")
+    check(lse, rl, lse_tol(c.dtype, rl), c.name + " lse")
+
+
 def boundary_rows(bos, eos, step=64, extra=()):
     rows = set()
     for t in range(bos, eos, step):
