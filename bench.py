@@ -20,6 +20,9 @@ Also reported on the same JSON line:
                 peak; the cache build is reported beside it;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores over a row
                 sample of the prefill workload, scaled to TFLOP/s.
+The roofline "traffic" fields are HBM bytes per launch measured with rocprof
+counters (profiles/hbm_traffic.json); they are null when the kernel sources
+no longer match the ones the counters were taken on.
 """
 from __future__ import annotations
 
@@ -42,9 +45,56 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-row-stride", type=int, default=16,
+    ap.add_argument("--cpu-row-stride", type=int, default=1,
                     help="oracle baseline evaluates every n-th query row")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain elementwise copy of 1 GiB (read) + 1 GiB (write), "
+                         "three times: the calibration kernel for rocprof's FETCH_SIZE / WRITE_SIZE")
     return ap.parse_args()
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "exact_attention_channel_amd", "csrc")
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.json")
+# sources whose kernels the recorded counters describe
+TRAFFIC_SOURCES = {
+    "attend": ["attn_fwd.hip", "common.h", "launch.h"],
+    "decode_split": ["decode.hip", "common.h", "launch.h"],
+}
+
+
+def sources_sha256(names):
+    import hashlib
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(key):
+    """HBM bytes per launch of kernel `key` from rocprof FETCH_SIZE + WRITE_SIZE
+    (scaled by the copy-kernel calibration), or None when no counters were
+    recorded or the kernel source changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["kernels"][key]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("sources_sha256") != sources_sha256(TRAFFIC_SOURCES[key]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def copy_probe():
+    import torch
+    n = 1 << 28  # float32 elements: 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"[bench] copy probe: 3 x elementwise copy of {n * 4} bytes read + {n * 4} bytes written")
 
 
 def causal_pairs(lengths, window=0):
@@ -82,6 +132,10 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
               "this library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
     import exact_attention_channel_amd as wa
@@ -163,7 +217,7 @@ def main():
         "roofline": {"kernel": "k_attn_fwd_bf16 (wall_attn_fwd_attend)", "bound": "mfma",
                      "achieved": round(attn_tflops, 2), "peak": PEAK_MFMA_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_MFMA_TFLOPS, 4),
-                     "traffic": None, "kernel_ms": round(ms_attn, 4)},
+                     "traffic": recorded_traffic("attend"), "kernel_ms": round(ms_attn, 4)},
         "prefill_breakdown_ms": {"prepare": round(ms_prep, 4), "attend": round(ms_attn, 4)},
     }
 
@@ -218,7 +272,8 @@ def main():
             "ms_per_call": round(dms, 4), "bytes_per_call": dbytes,
             "roofline": {"kernel": "k_decode_split + k_decode_combine (wall_attn_decode)",
                          "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "traffic": recorded_traffic("decode_split")},
             "cache_build": {"ms": round(build_ms, 3),
                             "GB/s": round(build_bytes / (build_ms * 1e-3) / 1e9, 1)},
         }
