@@ -363,11 +363,12 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
     return half_max(m);
   };
 
-  // Softmax with a per-row reference max instead of a running one.  Key
-  // tiles are visited newest first, so a row's reference is the max over its
-  // own diagonal tile (with decaying channels and a forget gate the newest
-  // keys carry the largest scores); every later tile is summed against that
-  // fixed reference and the output accumulators are never rescaled.  A tile
+  // Softmax with a per-row reference max instead of a running one.  The
+  // query tile's own key tiles are visited first, newest first, so a row's
+  // reference is the max over its diagonal tile (with decaying channels and a
+  // forget gate the newest keys carry the largest scores); every later tile
+  // is summed against that fixed reference and the output accumulators are
+  // never rescaled.  A tile
   // whose probabilities could exceed 2^64 against the reference (scores far
   // above the diagonal's) sets a flag; the workgroup then recomputes its rows
   // with the exact row max from a max-only sweep, which cannot overflow.
@@ -503,7 +504,10 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
   };
 
   // ---- pipeline ----
-  // Tiles are visited in the order J(t) = Jhi - t.  Iteration t: scores of
+  // Visiting order: the query tile's own QTILE/BK key tiles newest first,
+  // then the older tiles from the oldest up, so that workgroups running
+  // side by side walk the same key tiles together and find them in L2.
+  // Iteration t: scores of
   // tile t+1 (key buffer (t+1)&1) are accumulated while the softmax of tile t
   // runs, then tile t's probabilities meet its values (value buffer t&1).
   // Staging in the same iteration writes K_hat(t+2) into key buffer t&1 and
@@ -516,11 +520,12 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
   __shared__ int wg_ovf;
   if (tid == 0) wg_ovf = 0;
   const int NTL = Jhi - Jlo + 1;  // tiles of this workgroup
-  // mode 0: reference max from the newest tiles; 1: max-only sweep; 2: exact row max known
+  // mode 0: reference max from the diagonal tiles; 1: max-only sweep; 2: exact row max known
   auto sweep = [&](auto mode_c) {
     constexpr int MODE = decltype(mode_c)::value;
     constexpr bool VAL = MODE != 1;  // the pass needs values
-    auto tileJ = [&](int t) { return Jhi - t; };
+    const int ND = NTL < QTILE / BK ? NTL : QTILE / BK;  // diagonal tiles, visited first
+    auto tileJ = [&](int t) { return t < ND ? Jhi - t : Jlo + (t - ND); };
     auto stage_v_if = [&](int vbuf) {
       if (VAL) stage_v(vbuf);
     };
@@ -563,7 +568,7 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
     auto body = [&](int t, f32x16 (&Sc)[NQB], f32x16 (&Sn)[NQB]) {
       __syncthreads();
       const int buf = t & 1, nbuf = buf ^ 1;
-      const int J = tileJ(t), Jn = J - 1;
+      const int J = tileJ(t), Jn = tileJ(t + 1);
       const bool need_cur = J >= Jlo_w && J <= Jhi_w;
       const bool need_next = t + 1 < NTL && Jn >= Jlo_w && Jn <= Jhi_w;
       const int kj0 = J * BK;
