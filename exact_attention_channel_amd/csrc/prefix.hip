@@ -64,7 +64,7 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
 }
 
 // Phase A: sum of g (per channel) and of g_scalar over each chunk.
-// grid (NCmax, HQ, nseg), 256 threads.
+// grid (NCmax, HQ, nseg), 256 threads; a thread owns 4 channels.
 template <typename TE, int KD>
 __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
                                                     const TE *__restrict__ gs,
@@ -78,18 +78,30 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
   const int64_t r0 = bos + (int64_t)c * CHUNK;
   if (r0 >= eos) return;
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
-  constexpr int NG = 256 / KD;
-  const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
-  float acc = 0.f;
-  for (int r = grp; r < nrow; r += NG) acc += Elem<TE>::ld(g + ((r0 + r) * HQ + hq) * KD + n);
-  __shared__ float red[256];
-  red[threadIdx.x] = acc;
+  constexpr int NQ = KD / 4, NG = 256 / NQ;
+  const int q4 = threadIdx.x % NQ, grp = threadIdx.x / NQ;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int r = grp; r < nrow; r += NG) {
+    const float4 x = load4<TE>(g + ((r0 + r) * HQ + hq) * KD + 4 * q4);
+    acc.x += x.x;
+    acc.y += x.y;
+    acc.z += x.z;
+    acc.w += x.w;
+  }
+  __shared__ float4 red[NG][NQ];
+  red[grp][q4] = acc;
   __syncthreads();
   const int64_t cidx = (int64_t)s * NCmax + c;
   if (grp == 0) {
 #pragma unroll
-    for (int q = 1; q < NG; ++q) acc += red[q * KD + n];
-    csum[(cidx * HQ + hq) * KD + n] = acc;
+    for (int q = 1; q < NG; ++q) {
+      const float4 y = red[q][q4];
+      acc.x += y.x;
+      acc.y += y.y;
+      acc.z += y.z;
+      acc.w += y.w;
+    }
+    *reinterpret_cast<float4 *>(csum + (cidx * HQ + hq) * KD + 4 * q4) = acc;
   }
   if (gs != nullptr && threadIdx.x < 64) {
     float a = (int)threadIdx.x < nrow ? Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.f;
@@ -147,6 +159,47 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
   }
 }
 
+// In-chunk running sums of g for 4 channels of one chunk (shared by the two
+// phase-C kernels): rows are split into NG groups of RPG consecutive rows;
+// each thread scans its group, the group totals go through LDS.  Returns in
+// p2[i] the running sum at row grp*RPG + i in log2 units (offset included).
+template <typename TE, int KD>
+struct ChunkScan {
+  static constexpr int NQ = KD / 4, NG = 256 / NQ, RPG = CHUNK / NG;
+  __device__ __forceinline__ static void run(const TE *g, int64_t r0, int nrow, int HQ, int hq,
+                                             int q4, int grp, float4 base, float4 (&p2)[RPG]) {
+    __shared__ float4 tot[NG][NQ];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      const int r = grp * RPG + i;
+      p2[i] = r < nrow ? load4<TE>(g + ((r0 + r) * HQ + hq) * KD + 4 * q4)
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (i > 0) {
+        p2[i].x += p2[i - 1].x;
+        p2[i].y += p2[i - 1].y;
+        p2[i].z += p2[i - 1].z;
+        p2[i].w += p2[i - 1].w;
+      }
+    }
+    tot[grp][q4] = p2[RPG - 1];
+    __syncthreads();
+    for (int q = 0; q < grp; ++q) {
+      const float4 y = tot[q][q4];
+      base.x += y.x;
+      base.y += y.y;
+      base.z += y.z;
+      base.w += y.w;
+    }
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      p2[i].x = (base.x + p2[i].x) * LOG2E;
+      p2[i].y = (base.y + p2[i].y) * LOG2E;
+      p2[i].z = (base.z + p2[i].z) * LOG2E;
+      p2[i].w = (base.w + p2[i].w) * LOG2E;
+    }
+  }
+};
+
 // Phase C for the prefill: in-chunk running sums, then
 //   q_hat = q * 2^(P2 - RQ) * qscale   (RQ: anchor of the first chunk of the
 //                                       128-row query tile, so |P2 - RQ| is
@@ -154,7 +207,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
 //   k_tilde = k * 2^(R_c - P2)         (R_c: anchor of this 64-token chunk)
 // written in the operand type (IEEE half for bf16 inputs, float for fp32).
 //   gsum = running sum of g_scalar in log2 units.
-// grid (NCmax, HQ, nseg), 256 threads.
+// grid (NCmax, HQ, nseg), 256 threads; a thread owns 4 channels.
 template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
 __global__ __launch_bounds__(256) void k_prefill_operands(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ g,
@@ -169,36 +222,33 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   if (r0 >= eos) return;
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
   const int h = hq / (HQ / H);
-  constexpr int NG = 256 / KD;
-  constexpr int RPG = CHUNK / NG;
-  const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
-  float gv[RPG];
-#pragma unroll
-  for (int i = 0; i < RPG; ++i) {
-    const int r = grp * RPG + i;
-    gv[i] = r < nrow ? Elem<TE>::ld(g + ((r0 + r) * HQ + hq) * KD + n) : 0.f;
-  }
-#pragma unroll
-  for (int i = 1; i < RPG; ++i) gv[i] += gv[i - 1];
-  __shared__ float tot[NG][KD];
-  tot[grp][n] = gv[RPG - 1];
-  __syncthreads();
+  typedef ChunkScan<TE, KD> CS;
+  const int q4 = threadIdx.x % CS::NQ, grp = threadIdx.x / CS::NQ;
   const int64_t cidx = (int64_t)s * NCmax + c;
   const int64_t cq = (int64_t)s * NCmax + (c & ~1);
-  float base = off[(cidx * HQ + hq) * KD + n];
-  for (int q2 = 0; q2 < grp; ++q2) base += tot[q2][n];
-  const float A = anch[(cidx * HQ + hq) * KD + n];
-  const float RQ = anch[(cq * HQ + hq) * KD + n];
+  const float4 base = *reinterpret_cast<const float4 *>(off + (cidx * HQ + hq) * KD + 4 * q4);
+  const float4 A = *reinterpret_cast<const float4 *>(anch + (cidx * HQ + hq) * KD + 4 * q4);
+  const float4 RQ = *reinterpret_cast<const float4 *>(anch + (cq * HQ + hq) * KD + 4 * q4);
+  float4 p2[CS::RPG];
+  CS::run(g, r0, nrow, HQ, hq, q4, grp, base, p2);
 #pragma unroll
-  for (int i = 0; i < RPG; ++i) {
-    const int r = grp * RPG + i;
+  for (int i = 0; i < CS::RPG; ++i) {
+    const int r = grp * CS::RPG + i;
     if (r < nrow) {
       const int64_t t = r0 + r;
-      const float P2 = (base + gv[i]) * LOG2E;
-      const float qv = Elem<TE>::ld(q + (t * HQ + hq) * KD + n);
-      const float kv = Elem<TE>::ld(k + (t * H + h) * KD + n);
-      Elem<TO>::st(qh + (t * HQ + hq) * KD + n, qv * fast_exp2(P2 - RQ) * qscale);
-      Elem<TO>::st(kt + (t * HQ + hq) * KD + n, kv * fast_exp2(A - P2));
+      const float4 qv = load4<TE>(q + (t * HQ + hq) * KD + 4 * q4);
+      const float4 kv = load4<TE>(k + (t * H + h) * KD + 4 * q4);
+      float4 qo, ko;
+      qo.x = qv.x * fast_exp2(p2[i].x - RQ.x) * qscale;
+      qo.y = qv.y * fast_exp2(p2[i].y - RQ.y) * qscale;
+      qo.z = qv.z * fast_exp2(p2[i].z - RQ.z) * qscale;
+      qo.w = qv.w * fast_exp2(p2[i].w - RQ.w) * qscale;
+      ko.x = kv.x * fast_exp2(A.x - p2[i].x);
+      ko.y = kv.y * fast_exp2(A.y - p2[i].y);
+      ko.z = kv.z * fast_exp2(A.z - p2[i].z);
+      ko.w = kv.w * fast_exp2(A.w - p2[i].w);
+      store4<TO>(qh + (t * HQ + hq) * KD + 4 * q4, qo);
+      store4<TO>(kt + (t * HQ + hq) * KD + 4 * q4, ko);
     }
   }
   if (gs != nullptr && threadIdx.x < 64) {
@@ -222,27 +272,16 @@ __global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
   const int64_t r0 = bos + (int64_t)c * CHUNK;
   if (r0 >= eos) return;
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
-  constexpr int NG = 256 / KD;
-  constexpr int RPG = CHUNK / NG;
-  const int n = threadIdx.x % KD, grp = threadIdx.x / KD;
-  float gv[RPG];
-#pragma unroll
-  for (int i = 0; i < RPG; ++i) {
-    const int r = grp * RPG + i;
-    gv[i] = r < nrow ? Elem<TE>::ld(g + ((r0 + r) * HQ + hq) * KD + n) : 0.f;
-  }
-#pragma unroll
-  for (int i = 1; i < RPG; ++i) gv[i] += gv[i - 1];
-  __shared__ float tot[NG][KD];
-  tot[grp][n] = gv[RPG - 1];
-  __syncthreads();
+  typedef ChunkScan<TE, KD> CS;
+  const int q4 = threadIdx.x % CS::NQ, grp = threadIdx.x / CS::NQ;
   const int64_t cidx = (int64_t)s * NCmax + c;
-  float base = off[(cidx * HQ + hq) * KD + n];
-  for (int q2 = 0; q2 < grp; ++q2) base += tot[q2][n];
+  const float4 base = *reinterpret_cast<const float4 *>(off + (cidx * HQ + hq) * KD + 4 * q4);
+  float4 p2[CS::RPG];
+  CS::run(g, r0, nrow, HQ, hq, q4, grp, base, p2);
 #pragma unroll
-  for (int i = 0; i < RPG; ++i) {
-    const int r = grp * RPG + i;
-    if (r < nrow) P2[((r0 + r) * HQ + hq) * KD + n] = (base + gv[i]) * LOG2E;
+  for (int i = 0; i < CS::RPG; ++i) {
+    const int r = grp * CS::RPG + i;
+    if (r < nrow) *reinterpret_cast<float4 *>(P2 + ((r0 + r) * HQ + hq) * KD + 4 * q4) = p2[i];
   }
 }
 
