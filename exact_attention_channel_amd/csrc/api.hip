@@ -51,6 +51,11 @@ int check_fwd_shape(int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int6
   const int64_t ntok = varlen ? T : B * T;
   if (nseg > 65535 || HQ > 65535 || (maxlen + 63) / 64 > (int64_t)1 << 30)
     return fail(WA_UNSUPPORTED, "problem too large for the launch grid");
+  // the bf16 attention kernel addresses one sequence's rescaled keys, values
+  // and gate sums with 32-bit byte offsets
+  if (dtype == WA_BF16 && maxlen * HQ * (K > V ? K : V) * 2 >= ((int64_t)1 << 31))
+    return fail(WA_UNSUPPORTED, "sequence of %lld tokens too long for bf16 (max_seqlen*HQ*max(K,V)*2 must be < 2^31)",
+                (long long)maxlen);
   if (p) {
     p->B = B; p->T = T; p->HQ = HQ; p->H = H; p->K = K; p->V = V;
     p->nseg = nseg; p->maxlen = maxlen; p->ntok = ntok; p->dtype = dtype;

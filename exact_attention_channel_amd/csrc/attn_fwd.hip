@@ -230,11 +230,17 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
 
   u32x4 kraw[KNP], vraw[VNP];
   float graw = 0.f, araw = 0.f;
+  // per-tile scalars through buffer resources: lane offset plus a scalar tile
+  // offset, rows past the sequence read zero (such keys are always masked)
+  const __amdgpu_buffer_rsrc_t gs_rs = make_rsrc(HAS_GS ? gs_b : gsum, HAS_GS ? (int64_t)L * HQ * 4 : 0);
+  const int nch = (L + CHUNK - 1) / CHUNK;
+  const __amdgpu_buffer_rsrc_t an_rs = make_rsrc(anch_b, (int64_t)nch * HQ * DK * 4);
   auto load_k = [&](int J) {
     const int soff = J * BK * qrow * 2;
 #pragma unroll
     for (int p = 0; p < KNP; ++p) kraw[p] = buf_load16(kt_rs, kgoff + p * KRP * qrow * 2, soff);
-    if (HAS_GS && x_role) graw = gs_b[(int64_t)min(J * BK + xr, L - 1) * HQ];
+    if (HAS_GS && x_role)
+      graw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gs_rs, xr * HQ * 4, J * BK * HQ * 4, 0));
   };
   auto load_v = [&](int J) {
     const int soff = J * BK * vrow * 2;
@@ -242,7 +248,8 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
     for (int p = 0; p < VNP; ++p) vraw[p] = buf_load16(v_rs, vgoff + p * VRP * vrow * 2, soff);
   };
   auto load_a = [&](int J) {  // anchor of the chunk holding key tile J
-    if (d_role) araw = anch_b[(int64_t)(J * BK / CHUNK) * HQ * DK + dn];
+    if (d_role)
+      araw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(an_rs, dn * 4, (J * BK / CHUNK) * HQ * DK * 4, 0));
   };
   auto produce_d = [&](int t, int J) {  // araw holds the anchor of tile J, the t-th visited
     const int slot = t & 1;

@@ -70,6 +70,11 @@ def test_fwd_rejects_bad_shapes(lib):
     assert fwd(lib, dtype=7) == 2
     assert fwd(lib, cu=FAKE, nseq=0, maxlen=64) == 1
     assert fwd(lib, cu=FAKE, nseq=2, maxlen=500) == 1       # max_seqlen > T
+    # bf16: one sequence's rescaled keys must fit 32-bit offsets
+    assert fwd(lib, T=1 << 19, HQ=16, H=4, K=128, V=128) == 2
+    assert b"too long" in lib.wall_attn_last_error()
+    assert lib.wall_attn_fwd_workspace_bytes(1, (1 << 19) - 64, 16, 4, 128, 128, 0, 0, 0) > 0
+    assert lib.wall_attn_fwd_workspace_bytes(1, 1 << 19, 16, 4, 128, 128, 0, 0, 1) > 0  # fp32: 64-bit
 
 
 def test_fwd_rejects_bad_pointers_and_workspace(lib):
