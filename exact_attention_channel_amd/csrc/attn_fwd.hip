@@ -264,28 +264,41 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
     if (lane == 0) Fsh[slot][wave] = big ? 1 : 0;
   };
   // K_hat = k_tilde * d_IJ of the t-th visited tile into key buffer kbuf;
-  // returns 2^sigma of the tile
-  auto stage_k = [&](int t, int kbuf) -> float {
+  // returns 2^sigma of the tile.  Two 32-key tiles of one anchor chunk share
+  // their factors: the second reuses them from registers (the factors of a
+  // tile are published only when its chunk differs from the previous tile's).
+  u32x4 dpk_keep = u32x4{0, 0, 0, 0};
+  float csg_keep = 1.f, inv_keep = 1.f;
+  int chunk_keep = -1;
+  auto stage_k = [&](int t, int kbuf, int chunk) -> float {
     const int slot = t & 1;
-    int big = 0;
+    u32x4 dpk = dpk_keep;
+    float csg = csg_keep, inv = inv_keep;
+    if (chunk != chunk_keep) {
+      int big = 0;
 #pragma unroll
-    for (int w = 0; w < NWV; ++w) big |= Fsh[slot][w];
-    u32x4 dpk;
-    float csg = 1.f, inv = 1.f;
-    if (!big) {
-      dpk = *reinterpret_cast<const u32x4 *>(&Dsh[slot][kcp * 8]);
-    } else {
-      float em = -INFINITY;
-      for (int n = 0; n < DK; ++n) em = fmaxf(em, Esh[slot][n]);
-      const int sigma = (int)em - 8;
-      csg = __builtin_amdgcn_ldexpf(1.f, sigma);
-      inv = __builtin_amdgcn_ldexpf(1.f, -sigma);
+      for (int w = 0; w < NWV; ++w) big |= Fsh[slot][w];
+      csg = 1.f;
+      inv = 1.f;
+      if (!big) {
+        dpk = *reinterpret_cast<const u32x4 *>(&Dsh[slot][kcp * 8]);
+      } else {
+        float em = -INFINITY;
+        for (int n = 0; n < DK; ++n) em = fmaxf(em, Esh[slot][n]);
+        const int sigma = (int)em - 8;
+        csg = __builtin_amdgcn_ldexpf(1.f, sigma);
+        inv = __builtin_amdgcn_ldexpf(1.f, -sigma);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int e0 = max((int)Esh[slot][kcp * 8 + 2 * w] - sigma, -30);
-        const int e1 = max((int)Esh[slot][kcp * 8 + 2 * w + 1] - sigma, -30);
-        dpk[w] = pack_f16x2(__builtin_amdgcn_ldexpf(1.f, e0), __builtin_amdgcn_ldexpf(1.f, e1));
+        for (int w = 0; w < 4; ++w) {
+          const int e0 = max((int)Esh[slot][kcp * 8 + 2 * w] - sigma, -30);
+          const int e1 = max((int)Esh[slot][kcp * 8 + 2 * w + 1] - sigma, -30);
+          dpk[w] = pack_f16x2(__builtin_amdgcn_ldexpf(1.f, e0), __builtin_amdgcn_ldexpf(1.f, e1));
+        }
       }
+      dpk_keep = dpk;
+      csg_keep = csg;
+      inv_keep = inv;
+      chunk_keep = chunk;
     }
     unsigned char *kb = Ksm[kbuf];
 #pragma unroll
@@ -533,6 +546,11 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
     constexpr bool VAL = MODE != 1;  // the pass needs values
     const int ND = NTL < QTILE / BK ? NTL : QTILE / BK;  // diagonal tiles, visited first
     auto tileJ = [&](int t) { return t < ND ? Jhi - t : Jlo + (t - ND); };
+    auto chunkOf = [&](int t) { return tileJ(t) * BK / CHUNK; };
+    // factors are published for a tile only when its chunk differs from the
+    // previous visited tile's (the staging reuses them otherwise)
+    auto new_chunk = [&](int t) { return t == 0 || chunkOf(t) != chunkOf(t - 1); };
+    chunk_keep = -1;
     auto stage_v_if = [&](int vbuf) {
       if (VAL) stage_v(vbuf);
     };
@@ -545,10 +563,10 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
     produce_d(0, tileJ(0));
     if (1 < NTL) load_a(tileJ(1));
     __syncthreads();
-    float cs_cur = stage_k(0, 0);
+    float cs_cur = stage_k(0, 0, chunkOf(0));
     stage_v_if(0);
     if (1 < NTL) {
-      produce_d(1, tileJ(1));
+      if (new_chunk(1)) produce_d(1, tileJ(1));
       load_k(tileJ(1));
       load_v_if(1);
     }
@@ -565,9 +583,9 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
       }
     }
     float cs_next = 1.f;
-    if (1 < NTL) cs_next = stage_k(1, 1);
+    if (1 < NTL) cs_next = stage_k(1, 1, chunkOf(1));
     if (2 < NTL) {
-      produce_d(2, tileJ(2));
+      if (new_chunk(2)) produce_d(2, tileJ(2));
       load_k(tileJ(2));
     }
     if (3 < NTL) load_a(tileJ(3));
@@ -611,10 +629,10 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
         if (need_next) s_mfma(Sn, nbuf, NKS - 1);  // after any change of the row reference
       }
       float cs_stage = 1.f;
-      if (t + 2 < NTL) cs_stage = stage_k(t + 2, buf);
+      if (t + 2 < NTL) cs_stage = stage_k(t + 2, buf, chunkOf(t + 2));
       if (t + 1 < NTL) stage_v_if(nbuf);
       if (t + 3 < NTL) {
-        produce_d(t + 3, tileJ(t + 3));
+        if (new_chunk(t + 3)) produce_d(t + 3, tileJ(t + 3));
         load_k(tileJ(t + 3));
       }
       if (t + 2 < NTL) load_v_if(t + 2);
