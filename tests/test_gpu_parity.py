@@ -92,6 +92,8 @@ SMALL = [
         g_mode="neg_softplus", g_std=0.05, g_scalar_std=0.01, sink=True, window=77, seed=18),
     cfg("f32_varlen", 1, 0, 2, 1, 64, 64, torch.float32, nseq=6, len_lo=1, len_hi=200, seed=19),
     cfg("f32_T1", 1, 1, 2, 1, 64, 64, torch.float32, seed=20),
+    cfg("bf16_T450_D128_gqa8_gate_sink_window300", 1, 450, 8, 1, 128, 128, torch.bfloat16,
+        g_mode="neg_softplus", g_std=0.05, g_scalar_std=0.01, sink=True, window=300, seed=23),
 ]
 
 
@@ -102,6 +104,31 @@ def test_prefill_small_full(wa, c):
     ro, rl = run_oracle(x)
     check(o, ro, TOL[c.dtype], c.name + " o")
     check(lse, rl, lse_tol(c.dtype, rl), c.name + " lse")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_prefill_varlen_with_empty_sequences(wa, dtype):
+    """cu_seqlens with zero-length sequences first and in the middle."""
+    c = cfg("varlen_empty", 1, 0, 4, 2, 64, 64, dtype, nseq=9, len_lo=0, len_hi=90, window=33,
+            g_scalar_std=0.01, sink=True, seed=41)
+    x = W.make_prefill(c)
+    assert x["q"].shape[1] == 350
+    x["cu_seqlens"] = torch.tensor([0, 0, 13, 13, 13, 124, 141, 141, 292, 350], dtype=torch.int32)
+    o, lse = run_gpu(wa, x)
+    ro, rl = run_oracle(x)
+    check(o, ro, TOL[dtype], "varlen with empty sequences o")
+    check(lse, rl, lse_tol(dtype, rl), "varlen with empty sequences lse")
+
+
+def test_prefill_extreme_sink(wa):
+    """A sink logit far above (+25) or below (-25) every score."""
+    c = SMALL[1]
+    x = W.make_prefill(c)
+    x["sink_bias"] = torch.tensor([25.0, -25.0, 0.0, 5.0])
+    o, lse = run_gpu(wa, x)
+    ro, rl = run_oracle(x)
+    check(o, ro, TOL[c.dtype], "extreme sink o")
+    check(lse, rl, lse_tol(c.dtype, rl), "extreme sink lse")
 
 
 def test_config_tiny_fp32_full(wa):
