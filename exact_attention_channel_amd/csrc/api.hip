@@ -51,10 +51,13 @@ int check_fwd_shape(int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int6
   const int64_t ntok = varlen ? T : B * T;
   if (nseg > 65535 || HQ > 65535 || (maxlen + 63) / 64 > (int64_t)1 << 30)
     return fail(WA_UNSUPPORTED, "problem too large for the launch grid");
-  // the bf16 attention kernel addresses one sequence's rescaled keys, values
-  // and gate sums with 32-bit byte offsets
-  if (dtype == WA_BF16 && maxlen * HQ * (K > V ? K : V) * 2 >= ((int64_t)1 << 31))
-    return fail(WA_UNSUPPORTED, "sequence of %lld tokens too long for bf16 (max_seqlen*HQ*max(K,V)*2 must be < 2^31)",
+  // the bf16 attention kernel addresses one sequence's queries, values and
+  // gate sums (token-major) and one head's rescaled keys (K+16 channels per
+  // row) with 32-bit byte offsets
+  const int64_t row_bf16 = HQ * (K > V ? K : V) > K + 16 ? HQ * (K > V ? K : V) : K + 16;
+  if (dtype == WA_BF16 && maxlen * row_bf16 * 2 >= ((int64_t)1 << 31))
+    return fail(WA_UNSUPPORTED,
+                "sequence of %lld tokens too long for bf16 (max_seqlen*max(HQ*max(K,V), K+16)*2 must be < 2^31)",
                 (long long)maxlen);
   if (p) {
     p->B = B; p->T = T; p->HQ = HQ; p->H = H; p->K = K; p->V = V;

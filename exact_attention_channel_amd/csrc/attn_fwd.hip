@@ -6,8 +6,8 @@
 // window_size and cu_seqlens.  The pre-pass (prefix.hip) has already written
 //   q_hat_i   = q_i * 2^(P2_i - RQ_I) * scale * log2(e)     (query tile anchor RQ_I)
 //   k_tilde_j = k_j * 2^(R_J - P2_j)                        (key chunk anchor R_J)
-// so for a query tile I and a 64-key tile J the decayed scores are one dense
-// product: S = q_hat . (k_tilde * d_IJ)^T with d_IJ[n] = 2^(RQ_I[n] - R_J[n]),
+// so for a query tile I and a 64-key chunk J the decayed scores are one dense
+// product: S = (q_hat * d_IJ) . k_tilde^T with d_IJ[n] = 2^(RQ_I[n] - R_J[n]),
 // K exponentials per tile pair instead of K per (i, j) pair.  Scores are in
 // log2 units, so the online softmax (FlashAttention's running max and sum,
 // see the FlashAttention papers' tiling with rescaled partial outputs) uses
@@ -15,19 +15,22 @@
 //
 // bf16 inputs: the rescaled q/k operands are IEEE half (3 more mantissa bits
 // than bfloat16, which keeps the rounding of large decayed scores within
-// tolerance); P and V stay bfloat16.  If a key tile's inter-tile factor
-// d_IJ exceeds 2^8 (the decay sum grew between the key tile and the query
-// tile) the tile is staged as d_IJ * 2^-sigma with an integer sigma and the
-// scores are multiplied back by 2^sigma, so the half operands cannot
-// overflow; a channel pushed below the half range that way is smaller than
-// the dominant one by more than 2^20 and does not change the score.
+// tolerance); P and V stay bfloat16.  If a chunk's factor d_IJ exceeds 2^8
+// (the decay sum grew between the key chunk and the query tile) the query
+// operand takes d_IJ * 2^-sigma with an integer sigma and the scores are
+// multiplied back by 2^sigma, so the half operands cannot overflow; a
+// channel pushed below the half range that way is smaller than the dominant
+// one by more than 2^20 and does not change the score.
 //
-// Kernel layout: 256 threads = 4 waves x 32 query rows; per tile the workgroup
-// stages the decayed key tile (row-major) and the value tile (transposed) in
-// LDS.  Each wave computes S^T = K_hat Q_hat^T with v_mfma_f32_32x32x16_f16
-// so that a lane holds one query column: the row max and sum are in-lane
-// plus one swap between the two half-waves, and the probabilities feed the
-// next MFMA (O^T += V^T P^T, bf16) as its B operand without leaving registers.
+// Kernel layout: 256 threads = 4 waves x 32 query rows.  Key and value tiles
+// of 32 rows go from global memory straight into LDS (LDS-direct buffer
+// loads, no register staging); the decay factors sit on the query side, so
+// each wave rebuilds its half-precision query operand once per anchor chunk
+// from q_hat kept in LDS.  Each wave computes S^T = K_tilde Q'^T with
+// v_mfma_f32_32x32x16_f16 so that a lane holds one query column: the row max
+// and sum are in-lane plus one swap between the two half-waves, and the
+// probabilities feed the next MFMA (O^T += V^T P^T, bf16) as its B operand
+// without leaving registers; the value operand comes from transpose reads.
 // Tiles outside the causal / window / sequence range are never visited and
 // only boundary tiles are masked element by element (the block-sparse idea
 // of FlexAttention's BlockMask, computed from indices instead of stored).
@@ -102,48 +105,65 @@ template <int NS, int NP, int SA> struct FusedOrder {
   }
 };
 
-// NQB = 32-row query blocks per wave: 1 -> four waves of 32 rows, two waves
-// per SIMD (register budget 256); 2 -> two waves of 64 rows sharing every
-// staged operand between two blocks, one wave per SIMD (budget 512).
-template <int NQB> struct BfShape {
-  static constexpr int WQ = 32 * NQB;       // query rows per wave
-  static constexpr int NWV = QTILE / WQ;    // waves per workgroup
-  static constexpr int NTH = 64 * NWV;      // threads per workgroup
-  static constexpr int OCC = NQB == 1 ? 2 : 1;  // waves per SIMD
+// Tile geometry of the bf16 kernel for head sizes DK (scores) and DV (values).
+template <int DK, int DV> struct BfTile {
+  static constexpr int NWV = QTILE / 32;       // waves, 32 query rows each
+  static constexpr int NTH = 64 * NWV;         // threads per workgroup
+  static constexpr int KX = DK + 16;           // channels of a key row: decayed + one extra block
+  static constexpr int KRB = 2 * KX;           // bytes of a key row (global and LDS)
+  static constexpr int KPR = KRB / 16;         // 16-byte pieces per key row
+  static constexpr int VRB = 2 * DV;           // bytes of a value row in LDS
+  static constexpr int VPR = VRB / 16;         // 16-byte pieces per value row
+  static constexpr int QSB = 2 * DK + 16;      // LDS row stride of the query tile (bytes)
+  static constexpr int NKI = BK * KRB / 1024;  // LDS-direct loads per key tile
+  static constexpr int NVI = BK * VRB / 1024;  // LDS-direct loads per value tile
+  static_assert(NKI * 1024 == BK * KRB && NVI * 1024 == BK * VRB, "tiles must be whole KiB");
+  static_assert(KPR % 2 == 0, "key row swizzle pairs 16-byte pieces");
 };
 
-template <int DK, int DV, bool HAS_GS, int NQB>
-__global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_fwd_bf16(
+typedef __attribute__((address_space(3))) void lds_void;
+// LDS-direct 16-byte load: lane l of the wave writes LDS bytes dst + 16 l ..
+// dst + 16 l + 15 (one contiguous KiB per instruction) from its own buffer
+// offset; offsets outside the resource's extent write zeros.  Completion is
+// counted by vmcnt, so the issuing wave waits for it before the barrier that
+// hands the tile to the other waves.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *dst, int voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(__attribute__((address_space(3))) unsigned char *)dst,
+                                           16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void vm_wait0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
+
+template <int DK, int DV, bool HAS_GS>
+__global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     const _Float16 *__restrict__ qh, const _Float16 *__restrict__ kt, const bf16_t *__restrict__ v,
     const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
-    const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int nseg, int NCmax, int NQT,
-    int window) {
-  // Key tile rows hold DK decayed channels plus one extra 16-channel block
-  // that folds the softmax shift and the gate into the same MFMA:
-  //   extra channels of key j:   [2^-s, 2^-s, -Gs_j hi * 2^-s, -Gs_j lo * 2^-s, 0 ...]
-  //   extra channels of query i: [-m_i hi, -m_i lo, 1, 1, 0 ...]
-  // so the MFMA returns (score - running max) / 2^s directly (s = sigma of
-  // the tile, almost always 0) and the common path needs only the exp2.
-  constexpr int WQ = BfShape<NQB>::WQ, NWV = BfShape<NQB>::NWV, NTH = BfShape<NQB>::NTH;
-  constexpr int KX = DK + 16;            // channels per staged key row
-  constexpr int KSB = 2 * (KX + 8);      // LDS row stride of the key tile (bytes)
-  // LDS row stride of the value tile (bytes): 64 bytes of padding put the
-  // four rows of one transpose read, and the two 16-lane groups reading
-  // neighbouring columns, on disjoint banks
-  constexpr int VSB = 2 * DV + 64;
-  constexpr int NKS = KX / 16;           // MFMA k-steps of the score product
+    const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ, int H, int nseg, int NCmax,
+    int NQT, int window) {
+  // Score product per 32-key tile and wave: S^T = K_tilde Q'^T over DK + 16
+  // channels.  The key rows come from the pre-pass with their extra block
+  // [1, 1, -Gs_j hi, -Gs_j lo, 0 ...]; the wave's query operand Q' holds
+  // q_hat * d_IJ * 2^-s for the tile's anchor chunk and the extra block
+  // [-m_i hi * 2^-s, -m_i lo * 2^-s, 2^-s, 2^-s, 0 ...], so the MFMA returns
+  // (score - m_i - Gs_j) / 2^s directly (s = sigma of the chunk, almost
+  // always 0) and the common path needs only the exp2.
+  typedef BfTile<DK, DV> BT;
+  constexpr int NWV = BT::NWV, KRB = BT::KRB, VRB = BT::VRB, QSB = BT::QSB;
+  constexpr int NKS = BT::KX / 16;       // MFMA k-steps of the score product (last: extra block)
   constexpr int NMB = DV / 32;           // 32-channel blocks of the output
-  constexpr int KP = DK / 8, KRP = NTH / KP, KNP = BK / KRP;  // key staging: pieces, rows/pass, passes
-  constexpr int VP = DV / 8, VRP = NTH / VP, VNP = BK / VRP;  // value staging
-  constexpr int KS1 = 2;                 // score k-steps issued before the running-max check
-  __shared__ __attribute__((aligned(16))) unsigned char Ksm[2][BK * KSB];  // half
-  __shared__ __attribute__((aligned(16))) unsigned char Vsm[2][BK * VSB];  // bfloat16, row-major
-  __shared__ __attribute__((aligned(16))) uint16_t Dsh[2][DK];  // 2^e_n as half bits
-  __shared__ __attribute__((aligned(16))) float Esh[2][DK];     // e_n
-  __shared__ int Fsh[2][NWV];                                   // some e_n > 8 (per wave)
+  constexpr int CPL = DK / 64;           // channels per lane in the factor computation
+  // key tiles: rows of KRB bytes, 16-byte piece p of row r stored at piece
+  // p ^ ((r >> 3) & 1) (rows r and r + 8 then read disjoint banks);
+  // value tiles: rows of VRB bytes, 64-byte unit u of row r stored at unit
+  // u ^ vsw(r) (the four rows of one transpose read on disjoint banks)
+  __shared__ __attribute__((aligned(16))) unsigned char K0[BK * KRB], K1[BK * KRB];
+  __shared__ __attribute__((aligned(16))) unsigned char V0[BK * VRB], V1[BK * VRB];
+  __shared__ __attribute__((aligned(16))) unsigned char Qs[QTILE * QSB];  // q_hat of the tile, half
+  __shared__ __attribute__((aligned(16))) uint16_t Fq[NWV][DK];           // each wave's factors, half bits
+  __shared__ int wg_ovf;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index
   const int col = lane & 31, half = lane >> 5;
   const int hq = blockIdx.x % HQ;
   const int rest = blockIdx.x / HQ;
@@ -160,220 +180,204 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
   const int Jlo = (window > 0 ? max(0, i0 - window + 1) : 0) / BK;
   const int Jhi = i_last / BK;
 
-  // this wave's rows qw0 .. qw0 + 63 and the key tiles they see
-  const int qw0 = i0 + wave * WQ;
+  // this wave's rows qw0 .. qw0 + 31 and the key tiles they see
+  const int qw0 = i0 + wv * 32;
   const bool wave_live = qw0 < L;
-  const int qw_last = min(qw0 + WQ, L) - 1;
+  const int qw_last = min(qw0 + 32, L) - 1;
   const int Jlo_w = (window > 0 ? max(0, qw0 - window + 1) : 0) / BK;
   const int Jhi_w = wave_live ? qw_last / BK : -1;
 
   const int qrow = HQ * DK, vrow = H * DV;
-  const __amdgpu_buffer_rsrc_t kt_rs = make_rsrc(kt + (bos64 * HQ + hq) * DK, (int64_t)L * qrow * 2);
+  const __amdgpu_buffer_rsrc_t kt_rs = make_rsrc(kt + ((int64_t)hq * ntok + bos64) * BT::KX, (int64_t)L * KRB);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + (bos64 * H + h) * DV, (int64_t)L * vrow * 2);
-  const float *gs_b = HAS_GS ? gsum + bos64 * HQ + hq : nullptr;
 
-  // query operands: block qb holds rows qw0 + 32 qb + col
-  f16x8 qB[NQB][NKS];
-  float g_i[NQB];
+  // the wave's 32 rows of q_hat into LDS (read back once per anchor chunk)
   {
+    constexpr int QP = DK / 8;  // 16-byte pieces per query row
     const _Float16 *qh_b = qh + (bos64 * HQ + hq) * DK;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int r = qw0 + 32 * qb + col;
-      const int rr = r < L ? r : L - 1;
-      g_i[qb] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < DK / 16; ++ks)
-        qB[qb][ks] = *reinterpret_cast<const f16x8 *>(qh_b + (int64_t)rr * qrow + ks * 16 + half * 8);
-      if (HAS_GS && r < L) g_i[qb] = gs_b[(int64_t)r * HQ];
+    for (int k = 0; k < 32 * QP / 64; ++k) {
+      const int g = lane + 64 * k, rr = g / QP, pc = g % QP;
+      const int r = qw0 + rr;
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (r < L) x = *reinterpret_cast<const u32x4 *>(qh_b + (int64_t)r * qrow + 8 * pc);
+      *reinterpret_cast<u32x4 *>(&Qs[(wv * 32 + rr) * QSB + 16 * pc]) = x;
     }
   }
-  // the query's extra channels carry minus the row's reference max (log2
-  // units, relative to the row term Gs_i), split into two halves
-  auto set_qx = [&](int qb, float m) {
-    const _Float16 mh = (_Float16)(-m);
-    const _Float16 ml = (_Float16)(-m - (float)mh);
-    f16x8 x = f16x8{};
-    if (half == 0) {
-      x[0] = mh;
-      x[1] = ml;
-      x[2] = (_Float16)1.f;
-      x[3] = (_Float16)1.f;
-    }
-    qB[qb][NKS - 1] = x;
-  };
+  float g_i = 0.f;
+  if (HAS_GS && qw0 + col < L) g_i = gsum[(bos64 + qw0 + col) * HQ + hq];
 
-  // ---- staging roles (all threads) ----
-  const int kcp = tid % KP, kr0 = tid / KP;
-  const int kgoff = (kr0 * qrow + kcp * 8) * 2;
-  const int kloff = kr0 * KSB + kcp * 16;
-  const int vcp = tid % VP, vr0 = tid / VP;
-  const int vgoff = (vr0 * vrow + vcp * 8) * 2;
-  const int vloff = vr0 * VSB + vcp * 16;
-  constexpr int XPW = BK / NWV;                  // key rows whose extra channels each wave writes
-  const bool x_role = (tid & 63) < XPW;
-  const int xr = (tid >> 6) * XPW + (tid & 63);
-
-  // Tile-pair decay factors d_IJ[n] = 2^(RQ_I[n] - R_J[n]): the prefill
-  // anchors are integers, so the exponents are exact integers and the factors
-  // exact powers of two.  Thread n computes channel n of the tile two steps
-  // ahead; a flag per wave records an exponent above 8 (the decay sum rose
-  // between key tile and query tile), in which case the staging threads
-  // rebalance with an integer sigma = max_n e_n - 8: the staged operand is
-  // scaled by 2^-sigma and the scores by 2^sigma.
+  // Chunk decay factors d_IJ[n] = 2^(RQ_I[n] - R_J[n]): the prefill anchors
+  // are integers, so the exponents are exact integers and the factors exact
+  // powers of two.  Each wave computes all DK of them for its own use (CPL
+  // channels per lane).  If some exponent exceeds 8 (the decay sum rose
+  // between key chunk and query tile) the wave rebalances with an integer
+  // sigma = max_n e_n - 8: its query operand is scaled by 2^-sigma and the
+  // scores by 2^sigma, so the half operands cannot overflow.
   const int64_t cbase = (int64_t)seg * NCmax;
   const float *anch_b = anch + (cbase * HQ + hq) * DK;
-  constexpr int DPW = DK / NWV;                  // channels whose factor each wave computes
-  const bool d_role = lane < DPW;
-  const int dn = wave * DPW + lane;              // this thread's channel
-  const float rq = d_role ? anch_b[(int64_t)(2 * I) * HQ * DK + dn] : 0.f;  // query tile anchor
-
-  u32x4 kraw[KNP], vraw[VNP];
-  float graw = 0.f, araw = 0.f;
-  // per-tile scalars through buffer resources: lane offset plus a scalar tile
-  // offset, rows past the sequence read zero (such keys are always masked)
-  const __amdgpu_buffer_rsrc_t gs_rs = make_rsrc(HAS_GS ? gs_b : gsum, HAS_GS ? (int64_t)L * HQ * 4 : 0);
   const int nch = (L + CHUNK - 1) / CHUNK;
   const __amdgpu_buffer_rsrc_t an_rs = make_rsrc(anch_b, (int64_t)nch * HQ * DK * 4);
-  auto load_k = [&](int J) {
-    const int soff = J * BK * qrow * 2;
+  float rq[CPL], araw[CPL];
 #pragma unroll
-    for (int p = 0; p < KNP; ++p) kraw[p] = buf_load16(kt_rs, kgoff + p * KRP * qrow * 2, soff);
-    if (HAS_GS && x_role)
-      graw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(gs_rs, xr * HQ * 4, J * BK * HQ * 4, 0));
-  };
-  auto load_v = [&](int J) {
-    const int soff = J * BK * vrow * 2;
-#pragma unroll
-    for (int p = 0; p < VNP; ++p) vraw[p] = buf_load16(v_rs, vgoff + p * VRP * vrow * 2, soff);
-  };
-  auto load_a = [&](int J) {  // anchor of the chunk holding key tile J
-    if (d_role)
-      araw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(an_rs, dn * 4, (J * BK / CHUNK) * HQ * DK * 4, 0));
-  };
-  auto produce_d = [&](int t, int J) {  // araw holds the anchor of tile J, the t-th visited
-    const int slot = t & 1;
-    (void)J;
-    const float e = rq - araw;
-    if (d_role) {
-      const int ei = max((int)e, -30);
-      Dsh[slot][dn] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(1.f, ei));
-      Esh[slot][dn] = e;
+  for (int c = 0; c < CPL; ++c) {
+    rq[c] = anch_b[(int64_t)(2 * I) * HQ * DK + CPL * lane + c];  // query tile anchor
+    araw[c] = 0.f;
+  }
+  auto load_a = [&](int chunk) {  // anchors of a key chunk, this lane's channels
+    const int soff = chunk * HQ * DK * 4;
+    if (CPL == 2) {
+      const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(an_rs, lane * 8, soff, 0));
+      araw[0] = __uint_as_float(x[0]);
+      araw[CPL - 1] = __uint_as_float(x[1]);
+    } else {
+      araw[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(an_rs, lane * 4, soff, 0));
     }
-    const bool big = __ballot(d_role && e > 8.f) != 0;
-    if (lane == 0) Fsh[slot][wave] = big ? 1 : 0;
   };
-  // K_hat = k_tilde * d_IJ of the t-th visited tile into key buffer kbuf;
-  // returns 2^sigma of the tile.  Two 32-key tiles of one anchor chunk share
-  // their factors: the second reuses them from registers (the factors of a
-  // tile are published only when its chunk differs from the previous tile's).
-  u32x4 dpk_keep = u32x4{0, 0, 0, 0};
-  float csg_keep = 1.f, inv_keep = 1.f;
-  int chunk_keep = -1;
-  auto stage_k = [&](int t, int kbuf, int chunk) -> float {
-    const int slot = t & 1;
-    u32x4 dpk = dpk_keep;
-    float csg = csg_keep, inv = inv_keep;
-    if (chunk != chunk_keep) {
-      int big = 0;
-#pragma unroll
-      for (int w = 0; w < NWV; ++w) big |= Fsh[slot][w];
-      csg = 1.f;
-      inv = 1.f;
-      if (!big) {
-        dpk = *reinterpret_cast<const u32x4 *>(&Dsh[slot][kcp * 8]);
-      } else {
-        float em = -INFINITY;
-        for (int n = 0; n < DK; ++n) em = fmaxf(em, Esh[slot][n]);
-        const int sigma = (int)em - 8;
-        csg = __builtin_amdgcn_ldexpf(1.f, sigma);
-        inv = __builtin_amdgcn_ldexpf(1.f, -sigma);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int e0 = max((int)Esh[slot][kcp * 8 + 2 * w] - sigma, -30);
-          const int e1 = max((int)Esh[slot][kcp * 8 + 2 * w + 1] - sigma, -30);
-          dpk[w] = pack_f16x2(__builtin_amdgcn_ldexpf(1.f, e0), __builtin_amdgcn_ldexpf(1.f, e1));
-        }
-      }
-      dpk_keep = dpk;
-      csg_keep = csg;
-      inv_keep = inv;
-      chunk_keep = chunk;
+
+  // ---- query operand ----
+  f16x8 qB[NKS];
+  float inv_q = 1.f;  // 2^-sigma of the chunk whose factors qB holds
+  float m_ref = 0.f;  // the row's reference max (log2 units, relative to Gs_i)
+  // the query's extra channels carry minus the reference max, split into two
+  // halves, and the chunk's 2^-sigma for the key's 1 and gate channels
+  auto set_qx = [&]() {
+    const _Float16 mh = (_Float16)(-m_ref);
+    const _Float16 ml = (_Float16)(-m_ref - (float)mh);
+    f16x8 x = f16x8{};
+    if (half == 0) {
+      x[0] = (_Float16)((float)mh * inv_q);
+      x[1] = (_Float16)((float)ml * inv_q);
+      x[2] = (_Float16)inv_q;
+      x[3] = (_Float16)inv_q;
     }
-    unsigned char *kb = Ksm[kbuf];
+    qB[NKS - 1] = x;
+  };
+  // Publish the factors of the chunk whose anchors araw holds into the
+  // wave's Fq row (with the chunk's 2^-sigma in inv_pend); returns 2^sigma.
+  float inv_pend = 1.f;
+  auto factors = [&]() -> float {
+    float e[CPL];
+    bool big = false;
 #pragma unroll
-    for (int p = 0; p < KNP; ++p) {
-      u32x4 out;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        // copy the vector elements to scalars first: bit-casting an element
-        // expression directly has been seen to read element 0
-        const uint32_t kw = kraw[p][w], dw = dpk[w];
-        const f16x2 prod = __builtin_bit_cast(f16x2, kw) * __builtin_bit_cast(f16x2, dw);
-        out[w] = __builtin_bit_cast(uint32_t, prod);
-      }
-      *reinterpret_cast<u32x4 *>(kb + kloff + p * KRP * KSB) = out;
+    for (int c = 0; c < CPL; ++c) {
+      e[c] = rq[c] - araw[c];
+      big = big || e[c] > 8.f;
     }
-    if (x_role) {
-      u32x4 x = u32x4{0, 0, 0, 0};
-      x[0] = pack_f16x2(inv, inv);
-      if (HAS_GS) {
-        const float gsc = -graw * inv;
-        const _Float16 gh = (_Float16)gsc;
-        x[1] = pack_f16x2((float)gh, gsc - (float)gh);
-      }
-      *reinterpret_cast<u32x4 *>(kb + xr * KSB + DK * 2) = x;
+    int sigma = 0;
+    float csg = 1.f;
+    inv_pend = 1.f;
+    if (__ballot(big) != 0) {
+      float em = e[0];
+      if (CPL == 2) em = fmaxf(em, e[CPL - 1]);
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) em = fmaxf(em, __shfl_xor(em, d));
+      sigma = (int)em - 8;
+      csg = __builtin_amdgcn_ldexpf(1.f, sigma);
+      inv_pend = __builtin_amdgcn_ldexpf(1.f, -sigma);
+    }
+    if (CPL == 2) {
+      const int e0 = max((int)e[0] - sigma, -30), e1 = max((int)e[CPL - 1] - sigma, -30);
+      *reinterpret_cast<uint32_t *>(&Fq[wv][2 * lane]) =
+          pack_f16x2(__builtin_amdgcn_ldexpf(1.f, e0), __builtin_amdgcn_ldexpf(1.f, e1));
+    } else {
+      const int e0 = max((int)e[0] - sigma, -30);
+      Fq[wv][lane] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(1.f, e0));
     }
     return csg;
   };
-  auto stage_v = [&](int vbuf) {
-    unsigned char *vb = Vsm[vbuf];
+  // k-step ks of Q' from q_hat and the published factors
+  auto q_read = [&](int ks) {
+    return *reinterpret_cast<const f16x8 *>(&Qs[(wv * 32 + col) * QSB + 32 * ks + 16 * half]);
+  };
+  auto f_read = [&](int ks) { return *reinterpret_cast<const f16x8 *>(&Fq[wv][16 * ks + 8 * half]); };
+  auto rebuild = [&]() {
 #pragma unroll
-    for (int p = 0; p < VNP; ++p) *reinterpret_cast<u32x4 *>(vb + vloff + p * VRP * VSB) = vraw[p];
+    for (int ks = 0; ks < NKS - 1; ++ks) qB[ks] = q_read(ks) * f_read(ks);
+    inv_q = inv_pend;
+    set_qx();
+  };
+
+  // ---- LDS-direct staging: instruction i of a tile is issued by wave i % NWV ----
+  constexpr int NKM = (BT::NKI + NWV - 1) / NWV, NVM = (BT::NVI + NWV - 1) / NWV;
+  auto vsw = [](int r) { return NMB == 4 ? (r & 3) : ((r >> 1) & 1); };
+  int koff[NKM], voff[NVM];
+#pragma unroll
+  for (int m = 0; m < NKM; ++m) {
+    const int g = 64 * (wv + NWV * m) + lane, r = g / BT::KPR, pp = g % BT::KPR;
+    koff[m] = r * KRB + 16 * (pp ^ ((r >> 3) & 1));
+  }
+#pragma unroll
+  for (int m = 0; m < NVM; ++m) {
+    const int g = 64 * (wv + NWV * m) + lane, r = g / BT::VPR, pp = g % BT::VPR;
+    voff[m] = r * vrow * 2 + 16 * (4 * ((pp >> 2) ^ vsw(r)) + (pp & 3));
+  }
+  auto dma_k = [&](int J, unsigned char *buf) {
+#pragma unroll
+    for (int m = 0; m < NKM; ++m) {
+      const int i = wv + NWV * m;
+      if (i < BT::NKI) dma16(kt_rs, buf + 1024 * i, koff[m], J * BK * KRB);
+    }
+  };
+  auto dma_v = [&](int J, unsigned char *buf) {
+#pragma unroll
+    for (int m = 0; m < NVM; ++m) {
+      const int i = wv + NWV * m;
+      if (i < BT::NVI) dma16(v_rs, buf + 1024 * i, voff[m], J * BK * vrow * 2);
+    }
+  };
+  // the wave's d-th load of an iteration: key loads first, then value loads
+  constexpr int NDM = NKM + NVM;
+  auto dma_one = [&](int d, int Jk, unsigned char *kbuf, int Jv, unsigned char *vbuf, bool kdo, bool vdo) {
+    if (d < NKM) {
+      const int i = wv + NWV * d;
+      if (kdo && i < BT::NKI) dma16(kt_rs, kbuf + 1024 * i, koff[d], Jk * BK * KRB);
+    } else {
+      const int m = d - NKM, i = wv + NWV * m;
+      if (vdo && i < BT::NVI) dma16(v_rs, vbuf + 1024 * i, voff[m], Jv * BK * vrow * 2);
+    }
   };
 
   // ---- compute pieces ----
   // score A operand: key row col of the tile, channels 16 ks + 8 half .. +7
-  const int sa_off = col * KSB + half * 16;
-  auto s_mfma = [&](f32x16 (&S)[NQB], int kbuf, int ks) {
-    const f16x8 a = *reinterpret_cast<const f16x8 *>(&Ksm[kbuf][sa_off + ks * 32]);
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb)
-      S[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[qb][ks], S[qb], 0, 0, 0);
+  const int sa_off = col * KRB + 16 * (half ^ ((col >> 3) & 1));
+  auto s_mfma = [&](f32x16 &S, const unsigned char *Kb, int ks) {
+    const f16x8 a = *reinterpret_cast<const f16x8 *>(Kb + sa_off + ks * 32);
+    S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[ks], S, 0, 0, 0);
   };
   // The S^T accumulator holds, in lane (col, half), keys 8 (r/4) + 4 half + r%4
   // (r = 0..15) of query column col.  Its elements r = 8t..8t+7 are directly
   // the B operand (k = 16 keys) of the value product, with the keys in the
   // order k -> 8(k/4 % 2) + 4 half + k%4 within the 16-key step; the value
   // operand is read in the same order with two transpose reads (rows
-  // key0 .. key0+3 each).
-  const int j16 = lane & 15;
-  const int tr_off = (4 * half + (j16 >> 2)) * VSB + 2 * (16 * ((lane >> 4) & 1) + 4 * (j16 & 3));
-  f32x16 oacc[NQB][NMB];
-  auto pv = [&](int vbuf, const bf16x8 (&pB)[NQB][2]) {
+  // key0 .. key0+3 each).  tr_off[mb]: this lane's piece of output block mb
+  // in the first of those reads (rows 4 half + j16/4, unit mb swizzled).
+  const int j16 = lane & 15, x4 = j16 >> 2;
+  int tr_off[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+    tr_off[mb] = (4 * half + x4) * VRB + 64 * (mb ^ vsw(x4)) + 32 * ((lane >> 4) & 1) + 8 * (j16 & 3);
+  f32x16 oacc[NMB];
+  auto vread8 = [&](const unsigned char *Vb, int mb, int st) {
+    const unsigned char *base = Vb + tr_off[mb] + 16 * st * VRB;
+    const s16x4 a0 = lds_read_tr4(base), a1 = lds_read_tr4(base + 8 * VRB);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pv = [&](const unsigned char *Vb, const bf16x8 (&pB)[2]) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const unsigned char *base = &Vsm[vbuf][tr_off + 16 * s * VSB + 64 * mb];
-        const s16x4 a0 = lds_read_tr4(base), a1 = lds_read_tr4(base + 8 * VSB);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          oacc[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[qb][s], oacc[qb][mb], 0, 0, 0);
-      }
+      for (int s = 0; s < 2; ++s)
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread8(Vb, mb, s), pB[s], oacc[mb], 0, 0, 0);
   };
-  auto mask = [&](f32x16 (&S)[NQB], int kj0) {
+  auto mask = [&](f32x16 &S, int kj0) {
+    const int rel = qw0 + col - kj0 - 4 * half;  // allowed: kk <= rel
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const int rel = qw0 + 32 * qb + col - kj0 - 4 * half;  // allowed: kk <= rel
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + (r & 3);
-        bool ok = kk <= rel;
-        if (window > 0) ok = ok && (rel - kk < window);
-        S[qb][r] = ok ? S[qb][r] : -INFINITY;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int kk = 8 * (r >> 2) + (r & 3);
+      bool ok = kk <= rel;
+      if (window > 0) ok = ok && (rel - kk < window);
+      S[r] = ok ? S[r] : -INFINITY;
     }
   };
   auto tile_max = [&](const f32x16 &S) {
@@ -388,53 +392,41 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
   // reference is the max over its diagonal tile (with decaying channels and a
   // forget gate the newest keys carry the largest scores); every later tile
   // is summed against that fixed reference and the output accumulators are
-  // never rescaled.  A tile
-  // whose probabilities could exceed 2^64 against the reference (scores far
-  // above the diagonal's) sets a flag; the workgroup then recomputes its rows
-  // with the exact row max from a max-only sweep, which cannot overflow.
+  // never rescaled.  A tile whose probabilities could exceed 2^64 against
+  // the reference (scores far above the diagonal's) sets a flag; the
+  // workgroup then recomputes its rows with the exact row max from a
+  // max-only sweep, which cannot overflow.
   constexpr float PBIG = 0x1p64f;
-  float m_ref[NQB], l_part[NQB];  // l_part: this lane's half of each row's key sum
-  bool m_set[NQB];
-  bool all_set = false, ovf = false;
-  float m_true[NQB];
+  float l_part = 0.f;  // this lane's half of the row's key sum
+  bool m_set = false, all_set = false, ovf = false;
+  float m_true = -INFINITY;
+  auto tail = [&](f32x16 &S, bf16x8 (&pB)[2]) {
+    float rs = 0.f;
 #pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) m_true[qb] = -INFINITY;
-  auto tail = [&](f32x16 (&S)[NQB], bf16x8 (&pB)[NQB][2]) {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      float rs = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(S[qb][r]);
-        S[qb][r] = p;
-        rs += p;
-      }
-      l_part[qb] += rs;
-      ovf = ovf || !(rs <= PBIG);
-      pB[qb][0] = __builtin_convertvector(__builtin_shufflevector(S[qb], S[qb], 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
-      pB[qb][1] = __builtin_convertvector(__builtin_shufflevector(S[qb], S[qb], 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(S[r]);
+      S[r] = p;
+      rs += p;
     }
+    l_part += rs;
+    ovf = ovf || !(rs <= PBIG);
+    pB[0] = __builtin_convertvector(__builtin_shufflevector(S, S, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
+    pB[1] = __builtin_convertvector(__builtin_shufflevector(S, S, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
   };
   // rows without a reference yet take this tile's max (nothing is
   // accumulated for them, so nothing needs rescaling)
-  auto set_rows = [&](f32x16 (&S)[NQB]) {
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      const float mx = tile_max(S[qb]);
-      const bool take = !m_set[qb] && mx > -INFINITY;
-      const float shift = take ? mx : 0.f;
-      if (take) {
-        m_ref[qb] = mx;
-        m_set[qb] = true;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[qb][r] -= shift;
-      set_qx(qb, m_ref[qb]);
+  auto set_rows = [&](f32x16 &S) {
+    const float mx = tile_max(S);
+    const bool take = !m_set && mx > -INFINITY;
+    const float shift = take ? mx : 0.f;
+    if (take) {
+      m_ref = mx;
+      m_set = true;
     }
-    bool mine = true;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) mine = mine && m_set[qb];
-    all_set = __ballot(!mine) == 0;
+    for (int r = 0; r < 16; ++r) S[r] -= shift;
+    set_qx();
+    all_set = __ballot(!m_set) == 0;
   };
 
   // Steady-state tile in a fixed issue order (FusedOrder): scores of the next
@@ -442,102 +434,104 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
   // sched_barrier(0) keeps each slot's instructions together; the wave runs
   // its MFMA-dense part at raised priority so that the other wave on the SIMD
   // fills the gaps with its own VALU and LDS work.
-  auto fused = [&](f32x16 (&Sc)[NQB], f32x16 (&Sn)[NQB], int vbuf, int kbuf) {
+  // The block also issues the wave's LDS-direct loads of the next tiles (one
+  // per slot from slot DSLOT on) and, with RB, rebuilds each k-step of the
+  // query operand for the tile after next right after the score MFMA that
+  // last reads it, from the factors last published (the same values again
+  // when that tile's chunk is not new, so no branch is needed in the block).
+  auto fused = [&](auto rb_c, f32x16 &Sc, f32x16 &Sn, const unsigned char *Vb, const unsigned char *Kb,
+                   int Jk, unsigned char *kbuf, int Jv, unsigned char *vbuf, bool kdo) {
+    constexpr bool RB = decltype(rb_c)::value;
     constexpr int NP = 2 * NMB;
-    constexpr int SA = NQB == 1 ? 4 : 6;  // score slots before the first value slot
-    constexpr FusedOrder<NKS, NP, SA> FO{};
-    constexpr int KAHEAD = 4, VAHEAD = 3;
-    constexpr int E = 16 * NQB;           // exponentials of the tile
+    constexpr FusedOrder<NKS, NP, 4> FO{};
+    constexpr int KAHEAD = 4, VAHEAD = 3, RAHEAD = 2, DSLOT = 4;
+    constexpr int E = 16;                 // exponentials of the tile
+    static_assert(DSLOT + NDM <= FO.N, "every load needs a slot");
     f16x8 ka[NKS];
     bf16x8 va[NP];
-    auto kread = [&](int ks) {
-      ka[ks] = *reinterpret_cast<const f16x8 *>(&Ksm[kbuf][sa_off + ks * 32]);
+    f16x8 qr[NKS], fr[NKS];
+    auto kread = [&](int ks) { ka[ks] = *reinterpret_cast<const f16x8 *>(Kb + sa_off + ks * 32); };
+    auto vread = [&](int j) { va[j] = vread8(Vb, j % NMB, j / NMB); };  // block j % NMB, 16-key step j / NMB
+    auto rread = [&](int ks) {
+      if (RB && ks < NKS - 1) {
+        qr[ks] = q_read(ks);
+        fr[ks] = f_read(ks);
+      }
     };
-    auto vread = [&](int j) {  // value slot j: block mb = j % NMB, 16-key step st = j / NMB
-      const int mb = j % NMB, st = j / NMB;
-      const unsigned char *base = &Vsm[vbuf][tr_off + 16 * st * VSB + 64 * mb];
-      const s16x4 a0 = lds_read_tr4(base), a1 = lds_read_tr4(base + 8 * VSB);
-      va[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
-    // exponential e: 16-key step st = e / (8 NQB), block qb = e / 8 % NQB, element 8 st + e % 8
-    float pr[NQB][16];
-    bf16x8 pb[NQB][2];
-    float rs[NQB][2];
+    float pr[16];
+    bf16x8 pb[2];
+    float rs[2] = {0.f, 0.f};
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) rs[qb][0] = rs[qb][1] = 0.f;
-#pragma unroll
-    for (int i = 0; i < NKS; ++i)
+    for (int i = 0; i < NKS; ++i) {
       if (FO.slot_s[i] < KAHEAD) kread(i);
+      if (FO.slot_s[i] < RAHEAD) rread(i);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int n = 0; n < FO.N; ++n) {
 #pragma unroll
-      for (int i = 0; i < NKS; ++i)
+      for (int i = 0; i < NKS; ++i) {
         if (FO.slot_s[i] >= KAHEAD && FO.slot_s[i] - KAHEAD == n) kread(i);
+        if (FO.slot_s[i] >= RAHEAD && FO.slot_s[i] - RAHEAD == n) rread(i);
+      }
 #pragma unroll
       for (int j = 0; j < NP; ++j)
         if (FO.slot_p[j] - VAHEAD == n || (FO.slot_p[j] < VAHEAD && n == 0)) vread(j);
       if (n == FO.S_ALONE) __builtin_amdgcn_s_setprio(1);
       if (FO.kind[n] == 0) {
         const int ks = FO.idx[n];
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          Sn[qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks], qB[qb][ks], ks == 0 ? f32x16{} : Sn[qb], 0, 0, 0);
+        Sn = __builtin_amdgcn_mfma_f32_32x32x16_f16(ka[ks], qB[ks], ks == 0 ? f32x16{} : Sn, 0, 0, 0);
+        if (RB && ks < NKS - 1) qB[ks] = qr[ks] * fr[ks];
       } else {
         const int j = FO.idx[n], mb = j % NMB, st = j / NMB;
-#pragma unroll
-        for (int qb = 0; qb < NQB; ++qb)
-          oacc[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb[qb][st], oacc[qb][mb], 0, 0, 0);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb[st], oacc[mb], 0, 0, 0);
       }
+      if (n >= DSLOT && n - DSLOT < NDM) dma_one(n - DSLOT, Jk, kbuf, Jv, vbuf, kdo, true);
       if (n < FO.S_ALONE) {
         const int e0 = n * E / FO.S_ALONE, e1 = (n + 1) * E / FO.S_ALONE;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           if (e < e0 || e >= e1) continue;
-          const int st = e / (8 * NQB), qb = e / 8 % NQB, r = 8 * st + e % 8;
-          pr[qb][r] = fast_exp2(Sc[qb][r]);
-          rs[qb][r & 1] += pr[qb][r];
+          pr[e] = fast_exp2(Sc[e]);
+          rs[e & 1] += pr[e];
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st)
           if (e0 < E / 2 * (st + 1) && e1 >= E / 2 * (st + 1)) {
+            f32x8 p8;
 #pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) {
-              f32x8 p8;
-#pragma unroll
-              for (int r = 0; r < 8; ++r) p8[r] = pr[qb][8 * st + r];
-              pb[qb][st] = __builtin_convertvector(p8, bf16x8);
-            }
+            for (int r = 0; r < 8; ++r) p8[r] = pr[8 * st + r];
+            pb[st] = __builtin_convertvector(p8, bf16x8);
           }
         if (e1 == E) {
-#pragma unroll
-          for (int qb = 0; qb < NQB; ++qb) {
-            const float t = rs[qb][0] + rs[qb][1];
-            l_part[qb] += t;
-            ovf = ovf || !(t <= PBIG);
-          }
+          const float t = rs[0] + rs[1];
+          l_part += t;
+          ovf = ovf || !(t <= PBIG);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
+    if (RB) {
+      inv_q = inv_pend;
+      set_qx();
+    }
   };
 
   // ---- pipeline ----
   // Visiting order: the query tile's own QTILE/BK key tiles newest first,
   // then the older tiles from the oldest up, so that workgroups running
   // side by side walk the same key tiles together and find them in L2.
-  // Iteration t: scores of
-  // tile t+1 (key buffer (t+1)&1) are accumulated while the softmax of tile t
-  // runs, then tile t's probabilities meet its values (value buffer t&1).
-  // Staging in the same iteration writes K_hat(t+2) into key buffer t&1 and
-  // V(t+1) into value buffer (t+1)&1 from registers loaded one iteration
-  // earlier; one barrier per iteration orders it all.
-  if (x_role) {  // the unused half of the extra block stays zero
-    *reinterpret_cast<u32x4 *>(&Ksm[0][xr * KSB + DK * 2 + 16]) = u32x4{0, 0, 0, 0};
-    *reinterpret_cast<u32x4 *>(&Ksm[1][xr * KSB + DK * 2 + 16]) = u32x4{0, 0, 0, 0};
-  }
-  __shared__ int wg_ovf;
+  // Iteration t: scores of tile t+1 (key buffer (t+1)&1) are accumulated
+  // while the softmax of tile t runs, then tile t's probabilities meet its
+  // values (value buffer t&1).  After the iteration's barrier each wave
+  // issues its share of the LDS-direct loads of key tile t+2 (into key
+  // buffer t&1, free once tile t's scores are done) and value tile t+1 (into
+  // value buffer (t+1)&1), and the anchors of tile t+3's chunk; if tile t+2
+  // starts a new chunk, its factors (anchors from the previous iteration)
+  // are published first and the query operand is rebuilt as soon as tile
+  // t+1's scores no longer need it.  The wave's loads are waited for before
+  // the next barrier.
   if (tid == 0) wg_ovf = 0;
   const int NTL = Jhi - Jlo + 1;  // tiles of this workgroup
   // mode 0: reference max from the diagonal tiles; 1: max-only sweep; 2: exact row max known
@@ -547,115 +541,103 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
     const int ND = NTL < QTILE / BK ? NTL : QTILE / BK;  // diagonal tiles, visited first
     auto tileJ = [&](int t) { return t < ND ? Jhi - t : Jlo + (t - ND); };
     auto chunkOf = [&](int t) { return tileJ(t) * BK / CHUNK; };
-    // factors are published for a tile only when its chunk differs from the
-    // previous visited tile's (the staging reuses them otherwise)
     auto new_chunk = [&](int t) { return t == 0 || chunkOf(t) != chunkOf(t - 1); };
-    chunk_keep = -1;
-    auto stage_v_if = [&](int vbuf) {
-      if (VAL) stage_v(vbuf);
-    };
-    auto load_v_if = [&](int t) {
-      if (VAL) load_v(tileJ(t));
-    };
-    load_k(tileJ(0));
-    load_v_if(0);
-    load_a(tileJ(0));
-    produce_d(0, tileJ(0));
-    if (1 < NTL) load_a(tileJ(1));
-    __syncthreads();
-    float cs_cur = stage_k(0, 0, chunkOf(0));
-    stage_v_if(0);
-    if (1 < NTL) {
-      if (new_chunk(1)) produce_d(1, tileJ(1));
-      load_k(tileJ(1));
-      load_v_if(1);
+    if (MODE != 0) __syncthreads();  // the previous sweep's reads of the tile buffers are done
+    load_a(chunkOf(0));
+    dma_k(tileJ(0), K0);
+    if (VAL) dma_v(tileJ(0), V0);
+    if (1 < NTL) dma_k(tileJ(1), K1);
+    float cs_cur = factors();
+    rebuild();
+    const bool nc1 = 1 < NTL && new_chunk(1);
+    float cs_next = cs_cur;
+    if (nc1) {
+      load_a(chunkOf(1));
+      cs_next = factors();
     }
-    if (2 < NTL) load_a(tileJ(2));
+    if (2 < NTL && new_chunk(2)) load_a(chunkOf(2));
+    vm_wait0();
     __syncthreads();
-    f32x16 Sa[NQB], Sb[NQB];
+    f32x16 Sa, Sb;
     {
       const int J = tileJ(0);
       if (J >= Jlo_w && J <= Jhi_w) {
+        Sa = f32x16{};
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) Sa[qb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s_mfma(Sa, 0, ks);
+        for (int ks = 0; ks < NKS; ++ks) s_mfma(Sa, K0, ks);
       }
     }
-    float cs_next = 1.f;
-    if (1 < NTL) cs_next = stage_k(1, 1, chunkOf(1));
-    if (2 < NTL) {
-      if (new_chunk(2)) produce_d(2, tileJ(2));
-      load_k(tileJ(2));
-    }
-    if (3 < NTL) load_a(tileJ(3));
+    if (nc1) rebuild();
 
-    auto body = [&](int t, f32x16 (&Sc)[NQB], f32x16 (&Sn)[NQB]) {
+    auto body = [&](auto par_c, int t, f32x16 &Sc, f32x16 &Sn) {
+      constexpr int P = decltype(par_c)::value;  // t & 1
+      unsigned char *const Kc = P ? K1 : K0;     // key buffer of tiles t and t+2
+      unsigned char *const Kn = P ? K0 : K1;     // key buffer of tile t+1
+      unsigned char *const Vc = P ? V1 : V0;     // value buffer of tile t
+      unsigned char *const Vn = P ? V0 : V1;     // value buffer of tile t+1
       __syncthreads();
-      const int buf = t & 1, nbuf = buf ^ 1;
+      // factors of tile t+2's chunk (anchors loaded one iteration earlier),
+      // applied to the query operand once tile t+1's scores are issued
+      const bool nc2 = t + 2 < NTL && new_chunk(t + 2);
+      float cs2 = cs_next;
+      if (nc2) cs2 = factors();
+      if (t + 3 < NTL && new_chunk(t + 3)) load_a(chunkOf(t + 3));
       const int J = tileJ(t), Jn = tileJ(t + 1);
       const bool need_cur = J >= Jlo_w && J <= Jhi_w;
       const bool need_next = t + 1 < NTL && Jn >= Jlo_w && Jn <= Jhi_w;
       const int kj0 = J * BK;
-      const bool masked = kj0 + BK - 1 > qw0 || (window > 0 && qw0 + WQ - 1 - kj0 >= window);
-      bf16x8 pB[NQB][2];
+      const bool masked = kj0 + BK - 1 > qw0 || (window > 0 && qw0 + 31 - kj0 >= window);
+      bf16x8 pB[2];
       const bool general = masked || cs_cur != 1.f || (MODE == 0 && !all_set);
       if (MODE != 1 && need_cur && need_next && !general) {
-        // steady state: one block of score MFMAs, exponentials and value MFMAs
-        fused(Sc, Sn, buf, nbuf);
+        // steady state: one block of score MFMAs, exponentials and value
+        // MFMAs, with the next tiles' loads and the operand rebuild inside
+        const int Jk = t + 2 < NTL ? tileJ(t + 2) : 0;
+        // anchor chunks are two tiles long and start at even t unless a
+        // window or a short sequence shifts them: even iterations rebuild
+        // inside the block (always, the rebuild is idempotent), odd ones
+        // after it when their tile t+2 starts a chunk
+        fused(std::integral_constant<bool, P == 0>{}, Sc, Sn, Vc, Kn, Jk, Kc, Jn, Vn, t + 2 < NTL);
+        if (P == 1 && nc2) rebuild();
       } else {
+        if (t + 2 < NTL) dma_k(tileJ(t + 2), Kc);
+        if (VAL && t + 1 < NTL) dma_v(Jn, Vn);
         if (need_next) {
+          Sn = f32x16{};
 #pragma unroll
-        for (int qb = 0; qb < NQB; ++qb) Sn[qb] = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < NKS - 1; ++ks) s_mfma(Sn, nbuf, ks);
+          for (int ks = 0; ks < NKS - 1; ++ks) s_mfma(Sn, Kn, ks);
         }
         if (need_cur) {
           __asm__ volatile("s_nop 0");  // keep this a branch
           if (masked) mask(Sc, kj0);
-          if (cs_cur != 1.f) {
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) Sc[qb] *= cs_cur;
-          }
+          if (cs_cur != 1.f) Sc *= cs_cur;
           if (MODE == 1) {
-#pragma unroll
-            for (int qb = 0; qb < NQB; ++qb) m_true[qb] = fmaxf(m_true[qb], tile_max(Sc[qb]));
+            m_true = fmaxf(m_true, tile_max(Sc));
           } else {
             if (MODE == 0 && !all_set) set_rows(Sc);
             tail(Sc, pB);
-            pv(buf, pB);
+            pv(Vc, pB);
           }
         }
-        if (need_next) s_mfma(Sn, nbuf, NKS - 1);  // after any change of the row reference
+        if (need_next) s_mfma(Sn, Kn, NKS - 1);  // after any change of the row reference
+        if (nc2) rebuild();
       }
-      float cs_stage = 1.f;
-      if (t + 2 < NTL) cs_stage = stage_k(t + 2, buf, chunkOf(t + 2));
-      if (t + 1 < NTL) stage_v_if(nbuf);
-      if (t + 3 < NTL) {
-        if (new_chunk(t + 3)) produce_d(t + 3, tileJ(t + 3));
-        load_k(tileJ(t + 3));
-      }
-      if (t + 2 < NTL) load_v_if(t + 2);
-      if (t + 4 < NTL) load_a(tileJ(t + 4));
       cs_cur = cs_next;
-      cs_next = cs_stage;
+      cs_next = cs2;
+      vm_wait0();
     };
     for (int t = 0; t < NTL; t += 2) {
-      body(t, Sa, Sb);
+      body(std::integral_constant<int, 0>{}, t, Sa, Sb);
       if (t + 1 >= NTL) break;
-      body(t + 1, Sb, Sa);
+      body(std::integral_constant<int, 1>{}, t + 1, Sb, Sa);
     }
   };
   auto reset = [&](bool known) {
+    m_ref = known ? (m_true > -INFINITY ? m_true : 0.f) : 0.f;
+    m_set = known;
+    l_part = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      m_ref[qb] = known ? (m_true[qb] > -INFINITY ? m_true[qb] : 0.f) : 0.f;
-      m_set[qb] = known;
-      l_part[qb] = 0.f;
-      set_qx(qb, m_ref[qb]);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) oacc[qb][mb] = f32x16{};
-    }
+    for (int mb = 0; mb < NMB; ++mb) oacc[mb] = f32x16{};
     all_set = known;
     ovf = false;
   };
@@ -666,8 +648,7 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
   if (wg_ovf) {
     // rare: recompute with the exact row max (a sweep for the max, then the
     // sum against it), so no tile can overflow
-#pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) set_qx(qb, 0.f);
+    m_ref = 0.f;
     sweep(std::integral_constant<int, 1>{});
     reset(true);
     sweep(std::integral_constant<int, 2>{});
@@ -675,30 +656,29 @@ __global__ __launch_bounds__(BfShape<NQB>::NTH, BfShape<NQB>::OCC) void k_attn_f
 
   // ---- epilogue ----
   // scores above are relative to the row term Gs[i] (g_i); restore it here
-#pragma unroll
-  for (int qb = 0; qb < NQB; ++qb) {
-    const int qi = qw0 + 32 * qb + col;
-    const float Zl = half_sum(l_part[qb]);
+  {
+    const int qi = qw0 + col;
+    const float Zl = half_sum(l_part);
     if (qi < L) {
-      float mf = m_ref[qb], Z = Zl;
+      float mf = m_ref, Z = Zl;
       if (sink != nullptr) {
-        const float s2 = sink[hq] * LOG2E - g_i[qb];
-        mf = fmaxf(m_ref[qb], s2);
-        Z = Zl * fast_exp2(m_ref[qb] - mf) + fast_exp2(s2 - mf);
+        const float s2 = sink[hq] * LOG2E - g_i;
+        mf = fmaxf(m_ref, s2);
+        Z = Zl * fast_exp2(m_ref - mf) + fast_exp2(s2 - mf);
       }
-      const float inv = fast_exp2(m_ref[qb] - mf) / Z;
+      const float inv = fast_exp2(m_ref - mf) / Z;
       bf16_t *orow = o + ((bos64 + qi) * HQ + hq) * DV;
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           u32x2 w;
-          w.x = pack_bf16x2(oacc[qb][mb][4 * j] * inv, oacc[qb][mb][4 * j + 1] * inv);
-          w.y = pack_bf16x2(oacc[qb][mb][4 * j + 2] * inv, oacc[qb][mb][4 * j + 3] * inv);
+          w.x = pack_bf16x2(oacc[mb][4 * j] * inv, oacc[mb][4 * j + 1] * inv);
+          w.y = pack_bf16x2(oacc[mb][4 * j + 2] * inv, oacc[mb][4 * j + 3] * inv);
           *reinterpret_cast<u32x2 *>(orow + mb * 32 + 8 * j + 4 * half) = w;
         }
       if (lse != nullptr && half == 0)
-        lse[(bos64 + qi) * HQ + hq] = (mf + g_i[qb] + log2f(Z)) * LN2;
+        lse[(bos64 + qi) * HQ + hq] = (mf + g_i + log2f(Z)) * LN2;
     }
   }
 }
@@ -818,18 +798,17 @@ hipError_t attn_bf16_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t 
   const int NCmax = (int)((p.maxlen + CHUNK - 1) / CHUNK);
   const int NQT = (int)((p.maxlen + QTILE - 1) / QTILE);
   const dim3 grid((unsigned)(NQT * p.nseg * p.HQ));
-  constexpr int NQB = 1;
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(BfShape<NQB>::NTH), 0, st, static_cast<const _Float16 *>(ws.qh),
+    hipLaunchKernelGGL(kern, grid, dim3(BfTile<DK, DV>::NTH), 0, st, static_cast<const _Float16 *>(ws.qh),
                        static_cast<const _Float16 *>(ws.kt), static_cast<const bf16_t *>(p.v),
                        ws.anch, ws.gsum, p.sink, static_cast<bf16_t *>(p.o), p.lse, p.cu, p.T,
-                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT,
+                       p.ntok, (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT,
                        (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0));
   };
   if (p.g_scalar != nullptr)
-    args(k_attn_fwd_bf16<DK, DV, true, NQB>);
+    args(k_attn_fwd_bf16<DK, DV, true>);
   else
-    args(k_attn_fwd_bf16<DK, DV, false, NQB>);
+    args(k_attn_fwd_bf16<DK, DV, false>);
   return hipGetLastError();
 }
 

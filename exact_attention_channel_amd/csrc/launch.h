@@ -31,7 +31,8 @@ struct FwdWorkspace {
   float *anch;     // [nseg*NCmax, HQ, K] chunk anchors (log2 units)
   float *csum_s;   // [nseg*NCmax, HQ] chunk sums / offsets of g_scalar
   void *qh;        // [ntok, HQ, K] rescaled queries (dtype)
-  void *kt;        // [ntok, HQ, K] rescaled keys (dtype)
+  void *kt;        // rescaled keys: bf16 path [HQ, ntok, K+16] half with extra
+                   // channels, fp32 path [ntok, HQ, K] float
   float *gsum;     // [ntok, HQ] running gate sum (log2 units)
 };
 

@@ -9,11 +9,13 @@
 //   exp(P_i - P_j) = 2^(P2_i - RQ_I) * 2^(RQ_I - R_J) * 2^(R_J - P2_j)
 // exactly, so this pass writes q_hat_i = q_i * 2^(P2_i - RQ_I) * scale/ln2 and
 // k_tilde_j = k_j * 2^(R_J - P2_j) once per token, and the attention kernel
-// multiplies one 64-key tile by the K factors 2^(RQ_I - R_J) per tile pair.
+// applies the K factors 2^(RQ_I - R_J) once per (query tile, key chunk) pair.
 //
 // The running sum along time is a three-phase chunked scan:
 //   A: per-chunk channel sums,  B: exclusive scan over chunks,  C: in-chunk
 //   inclusive sums plus the operand rescaling.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -207,14 +209,21 @@ struct ChunkScan {
 //   k_tilde = k * 2^(R_c - P2)         (R_c: anchor of this 64-token chunk)
 // written in the operand type (IEEE half for bf16 inputs, float for fp32).
 //   gsum = running sum of g_scalar in log2 units.
+// Half operands (bf16 inputs): k_tilde is stored head-major, [HQ, ntok, KD+16],
+// each row followed by 16 extra channels [1, 1, -G hi, -G lo, 0 ...] (G =
+// gsum of the token split into two halves, 0 without a gate), so a key tile
+// is one contiguous block and the attention kernel's score product also
+// subtracts the row shift and the gate.  Float operands keep [ntok, HQ, KD].
 // grid (NCmax, HQ, nseg), 256 threads; a thread owns 4 channels.
 template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
 __global__ __launch_bounds__(256) void k_prefill_operands(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ g,
     const TE *__restrict__ gs, const float *__restrict__ off, const float *__restrict__ anch,
     const float *__restrict__ off_s, TO *__restrict__ qh, TO *__restrict__ kt,
-    float *__restrict__ gsum, const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int NCmax,
-    float qscale) {
+    float *__restrict__ gsum, const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ,
+    int H, int NCmax, float qscale) {
+  constexpr bool HM = std::is_same<TO, _Float16>::value;  // head-major rows with extras
+  constexpr int KX = HM ? KD + 16 : KD;
   const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
@@ -248,14 +257,25 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
       ko.z = kv.z * fast_exp2(A.z - p2[i].z);
       ko.w = kv.w * fast_exp2(A.w - p2[i].w);
       store4<TO>(qh + (t * HQ + hq) * KD + 4 * q4, qo);
-      store4<TO>(kt + (t * HQ + hq) * KD + 4 * q4, ko);
+      store4<TO>(kt + (HM ? (hq * ntok + t) : (t * HQ + hq)) * KX + 4 * q4, ko);
     }
   }
-  if (gs != nullptr && threadIdx.x < 64) {
+  if (threadIdx.x < 64) {
     const int r = threadIdx.x;
-    float x = r < nrow ? Elem<TE>::ld(gs + (r0 + r) * HQ + hq) : 0.f;
-    x = wave_inclusive_scan(x);
-    if (r < nrow) gsum[(r0 + r) * HQ + hq] = (off_s[cidx * HQ + hq] + x) * LOG2E;
+    float G = 0.f;
+    if (gs != nullptr) {
+      float x = r < nrow ? Elem<TE>::ld(gs + (r0 + r) * HQ + hq) : 0.f;
+      x = wave_inclusive_scan(x);
+      G = (off_s[cidx * HQ + hq] + x) * LOG2E;
+      if (r < nrow) gsum[(r0 + r) * HQ + hq] = G;
+    }
+    if (HM && r < nrow) {
+      const _Float16 gh = (_Float16)(-G);
+      u32x4 x0 = u32x4{pack_f16x2(1.f, 1.f), pack_f16x2((float)gh, -G - (float)gh), 0u, 0u};
+      u32x4 *dst = reinterpret_cast<u32x4 *>(kt + (hq * ntok + r0 + r) * KX + KD);
+      dst[0] = x0;
+      dst[1] = u32x4{0u, 0u, 0u, 0u};
+    }
   }
 }
 
@@ -335,7 +355,7 @@ hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStrea
                      static_cast<const TE *>(p.q), static_cast<const TE *>(p.k),
                      static_cast<const TE *>(p.g), gs, ws.csum, ws.anch, ws.csum_s,
                      static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt), ws.gsum, p.cu, p.T,
-                     (int)p.HQ, (int)p.H, NCmax, qscale);
+                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale);
   return hipGetLastError();
 }
 
@@ -376,7 +396,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
   char *anch = take(sizeof(float) * nchunk * p.HQ * p.K);
   char *csum_s = take(sizeof(float) * nchunk * p.HQ);
   char *qh = take(esz * p.ntok * p.HQ * p.K);
-  char *kt = take(esz * p.ntok * p.HQ * p.K);
+  char *kt = take(esz * p.ntok * p.HQ * (p.dtype == 0 ? p.K + 16 : p.K));
   char *gsum = take(sizeof(float) * p.ntok * p.HQ);
   if (ws) {
     ws->csum = reinterpret_cast<float *>(csum);

@@ -84,8 +84,9 @@ size_t wall_attn_fwd_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t H
  *   scale          host: multiplies the decayed dot product only; <= 0 means
  *                  K^-0.5.
  *   workspace      device buffer of at least wall_attn_fwd_workspace_bytes().
- * Supported: K, V in {64, 128}; for WA_BF16, max_seqlen*HQ*max(K,V)*2 < 2^31
- * (one sequence's rescaled keys addressed with 32-bit offsets).
+ * Supported: K, V in {64, 128}; for WA_BF16,
+ * max_seqlen*max(HQ*max(K,V), K+16)*2 < 2^31 (one sequence's operands
+ * addressed with 32-bit offsets).
  * Errors: INVALID_ARG for HQ % H != 0,
  * cu_seqlens with B != 1, non-positive sizes, NULL required pointers or
  * misaligned pointers; UNSUPPORTED for other K, V or dtype;
