@@ -112,8 +112,11 @@ template <int DK, int DV> struct BfTile {
   static constexpr int KX = DK + 16;           // channels of a key row: decayed + one extra block
   static constexpr int KRB = 2 * KX;           // bytes of a key row (global and LDS)
   static constexpr int KPR = KRB / 16;         // 16-byte pieces per key row
-  static constexpr int VRB = 2 * DV;           // bytes of a value row in LDS
-  static constexpr int VPR = VRB / 16;         // 16-byte pieces per value row
+  // bytes of a value row in LDS: 32 bytes of padding after the 2 DV data
+  // bytes (transpose reads of unpadded 256-byte rows, swizzled or not, run at
+  // about 60% of the padded rate)
+  static constexpr int VRB = 2 * DV + 32;
+  static constexpr int VPR = VRB / 16;         // 16-byte pieces per value row (the last two padding)
   static constexpr int QSB = 2 * DK + 16;      // LDS row stride of the query tile (bytes)
   static constexpr int NKI = BK * KRB / 1024;  // LDS-direct loads per key tile
   static constexpr int NVI = BK * VRB / 1024;  // LDS-direct loads per value tile
@@ -154,8 +157,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   constexpr int CPL = DK / 64;           // channels per lane in the factor computation
   // key tiles: rows of KRB bytes, 16-byte piece p of row r stored at piece
   // p ^ ((r >> 3) & 1) (rows r and r + 8 then read disjoint banks);
-  // value tiles: rows of VRB bytes, 64-byte unit u of row r stored at unit
-  // u ^ vsw(r) (the four rows of one transpose read on disjoint banks)
+  // value tiles: rows of VRB bytes (2 DV data bytes, then padding)
   __shared__ __attribute__((aligned(16))) unsigned char K0[BK * KRB], K1[BK * KRB];
   __shared__ __attribute__((aligned(16))) unsigned char V0[BK * VRB], V1[BK * VRB];
   __shared__ __attribute__((aligned(16))) unsigned char Qs[QTILE * QSB];  // q_hat of the tile, half
@@ -300,7 +302,6 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
 
   // ---- LDS-direct staging: instruction i of a tile is issued by wave i % NWV ----
   constexpr int NKM = (BT::NKI + NWV - 1) / NWV, NVM = (BT::NVI + NWV - 1) / NWV;
-  auto vsw = [](int r) { return NMB == 4 ? (r & 3) : ((r >> 1) & 1); };
   int koff[NKM], voff[NVM];
 #pragma unroll
   for (int m = 0; m < NKM; ++m) {
@@ -309,8 +310,9 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   }
 #pragma unroll
   for (int m = 0; m < NVM; ++m) {
+    // padding pieces load the row's first piece again (in range, never read)
     const int g = 64 * (wv + NWV * m) + lane, r = g / BT::VPR, pp = g % BT::VPR;
-    voff[m] = r * vrow * 2 + 16 * (4 * ((pp >> 2) ^ vsw(r)) + (pp & 3));
+    voff[m] = r * vrow * 2 + (pp < DV / 8 ? 16 * pp : 0);
   }
   auto dma_k = [&](int J, unsigned char *buf) {
 #pragma unroll
@@ -350,16 +352,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   // the B operand (k = 16 keys) of the value product, with the keys in the
   // order k -> 8(k/4 % 2) + 4 half + k%4 within the 16-key step; the value
   // operand is read in the same order with two transpose reads (rows
-  // key0 .. key0+3 each).  tr_off[mb]: this lane's piece of output block mb
-  // in the first of those reads (rows 4 half + j16/4, unit mb swizzled).
-  const int j16 = lane & 15, x4 = j16 >> 2;
-  int tr_off[NMB];
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb)
-    tr_off[mb] = (4 * half + x4) * VRB + 64 * (mb ^ vsw(x4)) + 32 * ((lane >> 4) & 1) + 8 * (j16 & 3);
+  // key0 .. key0+3 each).  tr_off: this lane's piece of the first of those
+  // reads (row 4 half + j16/4) for output block 0.
+  const int j16 = lane & 15;
+  const int tr_off = (4 * half + (j16 >> 2)) * VRB + 32 * ((lane >> 4) & 1) + 8 * (j16 & 3);
   f32x16 oacc[NMB];
   auto vread8 = [&](const unsigned char *Vb, int mb, int st) {
-    const unsigned char *base = Vb + tr_off[mb] + 16 * st * VRB;
+    const unsigned char *base = Vb + tr_off + 64 * mb + 16 * st * VRB;
     const s16x4 a0 = lds_read_tr4(base), a1 = lds_read_tr4(base + 8 * VRB);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
