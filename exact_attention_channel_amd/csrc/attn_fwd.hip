@@ -554,7 +554,8 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       load_a(chunkOf(1));
       cs_next = factors();
     }
-    if (2 < NTL && new_chunk(2)) load_a(chunkOf(2));
+    const bool nc2p = 2 < NTL && new_chunk(2);
+    if (nc2p) load_a(chunkOf(2));
     vm_wait0();
     __syncthreads();
     f32x16 Sa, Sb;
@@ -567,6 +568,8 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       }
     }
     if (nc1) rebuild();
+    float cs_next2 = cs_next;  // 2^sigma of the tile after next
+    if (nc2p) cs_next2 = factors();
 
     auto body = [&](auto par_c, int t, f32x16 &Sc, f32x16 &Sn) {
       constexpr int P = decltype(par_c)::value;  // t & 1
@@ -575,12 +578,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       unsigned char *const Vc = P ? V1 : V0;     // value buffer of tile t
       unsigned char *const Vn = P ? V0 : V1;     // value buffer of tile t+1
       __syncthreads();
-      // factors of tile t+2's chunk (anchors loaded one iteration earlier),
-      // applied to the query operand once tile t+1's scores are issued
+      // tile t+2's chunk factors were published at the end of the previous
+      // iteration; they reach the query operand once tile t+1's scores are
+      // issued.  The anchors of tile t+3's chunk load now and are published
+      // at the end of this iteration, while the tile loads complete.
       const bool nc2 = t + 2 < NTL && new_chunk(t + 2);
-      float cs2 = cs_next;
-      if (nc2) cs2 = factors();
-      if (t + 3 < NTL && new_chunk(t + 3)) load_a(chunkOf(t + 3));
+      const bool nc3 = t + 3 < NTL && new_chunk(t + 3);
+      if (nc3) load_a(chunkOf(t + 3));
       const int J = tileJ(t), Jn = tileJ(t + 1);
       const bool need_cur = J >= Jlo_w && J <= Jhi_w;
       const bool need_next = t + 1 < NTL && Jn >= Jlo_w && Jn <= Jhi_w;
@@ -621,8 +625,11 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
         if (need_next) s_mfma(Sn, Kn, NKS - 1);  // after any change of the row reference
         if (nc2) rebuild();
       }
+      float cs3 = cs_next2;
+      if (nc3) cs3 = factors();
       cs_cur = cs_next;
-      cs_next = cs2;
+      cs_next = cs_next2;
+      cs_next2 = cs3;
       vm_wait0();
     };
     for (int t = 0; t < NTL; t += 2) {
