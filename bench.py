@@ -120,6 +120,38 @@ def event_time_ms(fn, n, torch):
     return s.elapsed_time(e) / n
 
 
+def time_prefill(cfg, lib, wa, W, torch, dev, stream, steps, warmup):
+    """Event-timed wall_attn_fwd on one prefill workload: (ms per call, algorithmic FLOPs)."""
+    x = W.make_prefill(cfg, device=dev)
+    B, T = int(x["q"].shape[0]), int(x["q"].shape[1])
+    HQ, H, K, V = cfg.HQ, cfg.H, cfg.K, cfg.V
+    dt = wa.WA_BF16 if cfg.dtype == torch.bfloat16 else wa.WA_F32
+    cu = x["cu_seqlens"]
+    if cu is None:
+        nseq, maxlen, lengths = 0, 0, [T] * B
+    else:
+        lengths = (cu[1:] - cu[:-1]).tolist()
+        nseq, maxlen = len(lengths), max(lengths)
+    window = x["window_size"] or 0
+    o = torch.empty(B, T, HQ, V, dtype=cfg.dtype, device=dev)
+    wsb = lib.wall_attn_fwd_workspace_bytes(B, T, HQ, H, K, V, nseq, maxlen, dt)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+
+    def fwd():
+        rc = lib.wall_attn_fwd(ptr(x["q"]), ptr(x["k"]), ptr(x["v"]), ptr(x["g"]),
+                               ptr(x["g_scalar"]), ptr(x["sink_bias"]), ptr(o), None,
+                               B, T, HQ, H, K, V, ptr(cu), nseq, maxlen, window,
+                               float(x["scale"]), dt, ptr(ws), wsb, stream)
+        if rc:
+            raise RuntimeError(lib.wall_attn_last_error().decode())
+
+    for _ in range(warmup):
+        fwd()
+    ms = event_time_ms(fwd, steps, torch)
+    return ms, 2.0 * HQ * (K + V) * causal_pairs(lengths, window)
+
+
 def log(msg):
     sys.stderr.write(msg + "\n")
     sys.stderr.flush()
@@ -221,6 +253,27 @@ def main():
         "prefill_breakdown_ms": {"prepare": round(ms_prep, 4), "attend": round(ms_attn, 4)},
     }
 
+    # ------------------------------------------------------------ other workloads
+    # the remaining prefill workloads (tiny fp32, usage shape, packed varlen
+    # with a window), same protocol; their outputs are checked by the GPU tests
+    allc = []
+    for cfg in W.PREFILL_CONFIGS:
+        if cfg is c:
+            ms_c, fl_c = ms_step, flops
+        else:
+            ms_c, fl_c = time_prefill(cfg, lib, wa, W, torch, dev, stream, args.steps,
+                                      args.warmup)
+            torch.cuda.empty_cache()
+        tf = fl_c / (ms_c * 1e-3) / 1e12
+        e = {"workload": cfg.name, "call": "wall_attn_fwd",
+             "dtype": "bf16" if cfg.dtype == torch.bfloat16 else "f32",
+             "ms": round(ms_c, 4), "gflop": round(fl_c / 1e9, 3), "TFLOP/s": round(tf, 2)}
+        if cfg.dtype == torch.bfloat16:
+            e["frac_mfma_peak"] = round(tf / PEAK_MFMA_TFLOPS, 4)
+        log(f"[bench] {cfg.name}: {ms_c:.4f} ms, {tf:.1f} TFLOP/s")
+        allc.append(e)
+    out["all_configs"] = allc
+
     # ------------------------------------------------------------------ decode
     if not args.no_decode:
         d = W.DECODE_T32768_BF16
@@ -277,6 +330,9 @@ def main():
             "cache_build": {"ms": round(build_ms, 3),
                             "GB/s": round(build_bytes / (build_ms * 1e-3) / 1e9, 1)},
         }
+        out["all_configs"].append({"workload": d.name, "call": "wall_attn_decode", "dtype": "bf16",
+                                   "ms": round(dms, 4), "GB/s": round(gbs, 1),
+                                   "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
         del kt, rc_, y, dws, do, dl, pc
         torch.cuda.empty_cache()
 
