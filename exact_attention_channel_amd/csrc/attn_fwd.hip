@@ -318,14 +318,14 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
 #pragma unroll
     for (int m = 0; m < NKM; ++m) {
       const int i = wv + NWV * m;
-      if (i < BT::NKI) dma16(kt_rs, buf + 1024 * i, koff[m], J * BK * KRB);
+      if ((m + 1) * NWV <= BT::NKI || i < BT::NKI) dma16(kt_rs, buf + 1024 * i, koff[m], J * BK * KRB);
     }
   };
   auto dma_v = [&](int J, unsigned char *buf) {
 #pragma unroll
     for (int m = 0; m < NVM; ++m) {
       const int i = wv + NWV * m;
-      if (i < BT::NVI) dma16(v_rs, buf + 1024 * i, voff[m], J * BK * vrow * 2);
+      if ((m + 1) * NWV <= BT::NVI || i < BT::NVI) dma16(v_rs, buf + 1024 * i, voff[m], J * BK * vrow * 2);
     }
   };
   // the wave's d-th load of an iteration: key loads first, then value loads
@@ -333,10 +333,10 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   auto dma_one = [&](int d, int Jk, unsigned char *kbuf, int Jv, unsigned char *vbuf, bool kdo, bool vdo) {
     if (d < NKM) {
       const int i = wv + NWV * d;
-      if (kdo && i < BT::NKI) dma16(kt_rs, kbuf + 1024 * i, koff[d], Jk * BK * KRB);
+      if (kdo && ((d + 1) * NWV <= BT::NKI || i < BT::NKI)) dma16(kt_rs, kbuf + 1024 * i, koff[d], Jk * BK * KRB);
     } else {
       const int m = d - NKM, i = wv + NWV * m;
-      if (vdo && i < BT::NVI) dma16(v_rs, vbuf + 1024 * i, voff[m], Jv * BK * vrow * 2);
+      if (vdo && ((m + 1) * NWV <= BT::NVI || i < BT::NVI)) dma16(v_rs, vbuf + 1024 * i, voff[m], Jv * BK * vrow * 2);
     }
   };
 
@@ -539,7 +539,8 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     constexpr bool VAL = MODE != 1;  // the pass needs values
     const int ND = NTL < QTILE / BK ? NTL : QTILE / BK;  // diagonal tiles, visited first
     auto tileJ = [&](int t) { return t < ND ? Jhi - t : Jlo + (t - ND); };
-    auto chunkOf = [&](int t) { return tileJ(t) * BK / CHUNK; };
+    static_assert(CHUNK == 2 * BK, "a chunk is two key tiles");
+    auto chunkOf = [&](int t) { return tileJ(t) >> 1; };  // tile indices are never negative
     auto new_chunk = [&](int t) { return t == 0 || chunkOf(t) != chunkOf(t - 1); };
     if (MODE != 0) __syncthreads();  // the previous sweep's reads of the tile buffers are done
     load_a(chunkOf(0));
