@@ -82,13 +82,20 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
   constexpr int NQ = KD / 4, NG = 256 / NQ;
   const int q4 = threadIdx.x % NQ, grp = threadIdx.x / NQ;
+  // compile-time row count with a guard: the thread's loads go out together
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int r = grp; r < nrow; r += NG) {
-    const float4 x = load4<TE>(g + ((r0 + r) * HQ + hq) * KD + 4 * q4);
-    acc.x += x.x;
-    acc.y += x.y;
-    acc.z += x.z;
-    acc.w += x.w;
+  float4 xs[CHUNK / NG];
+#pragma unroll
+  for (int i = 0; i < CHUNK / NG; ++i) {
+    const int r = grp + i * NG;
+    xs[i] = r < nrow ? load4<TE>(g + ((r0 + r) * HQ + hq) * KD + 4 * q4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int i = 0; i < CHUNK / NG; ++i) {
+    acc.x += xs[i].x;
+    acc.y += xs[i].y;
+    acc.z += xs[i].z;
+    acc.w += xs[i].w;
   }
   __shared__ float4 red[NG][NQ];
   red[grp][q4] = acc;
@@ -143,9 +150,17 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
     p = csum_s + c0 * HQ + hq;
     stride = HQ;
   }
+  // the chunk sums are read in batches of 8 independent loads: one memory
+  // round trip per batch instead of one per chunk
   float tot = 0.f;
   if (active)
-    for (int c = cb; c < ce; ++c) tot += p[c * stride];
+    for (int c = cb; c < ce; c += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? p[(int64_t)(c + u) * stride] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) tot += x[u];
+    }
   __shared__ float part[8][32];
   part[grp][threadIdx.x & 31] = tot;
   __syncthreads();
@@ -153,11 +168,18 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
   float run = 0.f;
   for (int q = 0; q < grp; ++q) run += part[q][threadIdx.x & 31];
   float *a = anch + (c0 * HQ + hq) * KD + ch;
-  for (int c = cb; c < ce; ++c) {
-    const float x = p[c * stride];
-    p[c * stride] = run;
-    if (ch < KD) a[c * stride] = rintf((run + x) * LOG2E);
-    run += x;
+  for (int c = cb; c < ce; c += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? p[(int64_t)(c + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c + u < ce) {
+        p[(int64_t)(c + u) * stride] = run;
+        if (ch < KD) a[(int64_t)(c + u) * stride] = rintf((run + x[u]) * LOG2E);
+      }
+      run += x[u];
+    }
   }
 }
 
