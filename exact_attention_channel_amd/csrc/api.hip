@@ -216,6 +216,10 @@ int wall_attn_decode(const void *q, const void *v, const float *p_curr, const vo
   for (const void *ptr : ptrs)
     if (ptr && !aligned16(ptr)) return fail(WA_INVALID_ARG, "device pointers must be 16-byte aligned");
   if (B > 65535) return fail(WA_UNSUPPORTED, "B too large for the launch grid");
+  // the decode kernel addresses one batch row's k_tilde with 32-bit byte offsets
+  if (T_kv * HQ * K * (dtype == WA_BF16 ? 2 : 4) >= ((int64_t)1 << 31))
+    return fail(WA_UNSUPPORTED, "cache of %lld tokens too long (T_kv*HQ*K*operand bytes must be < 2^31)",
+                (long long)T_kv);
   const size_t need = wa::decode_workspace_size(B, T_kv, HQ, H, V);
   if (workspace_bytes < need)
     return fail(WA_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);

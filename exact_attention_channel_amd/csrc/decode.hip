@@ -18,6 +18,15 @@
 namespace wa {
 namespace {
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+  // integer select: HIP's min() on 64-bit integers goes through f64 VALU code
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+}
+
 template <typename TE>
 struct Vec8;  // 8 consecutive elements in registers
 template <>
@@ -33,6 +42,9 @@ template <>
 struct Vec8<_Float16> {
   u32x4 w;
   __device__ __forceinline__ void load(const _Float16 *p) { w = *reinterpret_cast<const u32x4 *>(p); }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    w = buf_load16(rs, voff, soff);
+  }
   __device__ __forceinline__ void zero() { w = u32x4{0, 0, 0, 0}; }
   __device__ __forceinline__ float operator[](int e) const {
     return (e & 1) ? f16_hi(w[e >> 1]) : f16_lo(w[e >> 1]);
@@ -45,6 +57,10 @@ struct Vec8<float> {
     a = *reinterpret_cast<const float4 *>(p);
     b = *reinterpret_cast<const float4 *>(p + 4);
   }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
+    a = __builtin_bit_cast(float4, buf_load16(rs, voff, soff));
+    b = __builtin_bit_cast(float4, buf_load16(rs, voff + 16, soff));
+  }
   __device__ __forceinline__ void zero() { a = b = make_float4(0.f, 0.f, 0.f, 0.f); }
   __device__ __forceinline__ float operator[](int e) const {
     const float4 &x = e < 4 ? a : b;
@@ -52,6 +68,27 @@ struct Vec8<float> {
     return i == 0 ? x.x : i == 1 ? x.y : i == 2 ? x.z : x.w;
   }
 };
+
+// Sum of x over groups of N consecutive lanes (N = 8 or 16) with DPP row
+// rotations; every lane of a group gets the group's sum.
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+  static_assert(N == 8 || N == 16, "groups of 8 or 16 lanes");
+  // row_ror:n has DPP control 0x120 + n; rotations stay inside 16-lane rows
+  if (N == 16) x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xf, 0xf, false));
+  if (N == 8) {
+    // rotations by 4, 2, 1 inside a 16-lane row mix the two 8-lane halves;
+    // use xor shuffles within 8 lanes instead
+    x += __shfl_xor(x, 4, 8);
+    x += __shfl_xor(x, 2, 8);
+    x += __shfl_xor(x, 1, 8);
+    return x;
+  }
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xf, 0xf, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xf, 0xf, false));
+  return x;
+}
 
 // grid (nsplit, HQ/NHB, B), 256 threads.  The cache holds k_tilde in the
 // operand type TK (IEEE half for bf16 inputs).
@@ -67,7 +104,6 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(
     float *__restrict__ part_ml, int64_t T, int HQ, int H, int NC, int nsplit, int cps,
     float qscale) {
   constexpr int C = CHUNK;
-  constexpr int KV8 = DK / 8;         // 8-element pieces of a key row
   constexpr int VCG = DV / 8;         // 8-channel groups of a value row
   constexpr int KL = 256 / VCG;       // key lanes in the PV phase
   constexpr int KPL = C / KL;         // keys per key lane
@@ -103,16 +139,28 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(
     }
   };
 
-  // score role: head sh = wave, key kk = lane.  Keys past T_kv are read at
-  // the last key (in bounds) and masked.
-  const int sh = wave, kk = lane;
+  // score role: head sh = wave.  Load i of a chunk brings keys 4 i + r
+  // (r = lane / 16), lane u = lane % 16 holding channels 8u .. 8u+7 of its
+  // key: each load instruction covers four whole 256-byte key rows.  The
+  // partial dot products are summed over the 16 lanes of a row, and lane
+  // (r, u) then owns key kk = 4u + r.  Key rows come through a buffer
+  // resource over this batch row and head (lane offset plus a scalar row
+  // offset per load); rows past T_kv read zero and are masked.
+  static_assert(DK == 128 || DK == 64, "key rows of 16 or 8 pieces");
+  constexpr int LPR = DK / 8;         // lanes per key row
+  constexpr int RPI = 64 / LPR;       // key rows per load instruction
+  constexpr int NKI = C / RPI;        // load instructions per chunk
+  const int sh = wave, kr = lane / LPR, ku = lane % LPR;
+  const int kk = RPI * ku + kr;       // the key whose score this lane keeps (NKI == LPR)
+  static_assert(NKI == LPR, "one reduced score per lane");
   const bool s_role = sh < NHB;
-  const TK *kt_row = kt + (tb * HQ + hq0 + (s_role ? sh : 0)) * DK;
-  auto kptr = [&](int c) {
-    const int64_t j = min((int64_t)c * C + kk, T - 1);
-    return kt_row + j * HQ * DK;
+  const __amdgpu_buffer_rsrc_t kt_rs =
+      make_rsrc(kt + (tb * HQ + hq0 + (s_role ? sh : 0)) * DK, T * HQ * DK * (int64_t)sizeof(TK));
+  const int k_voff = (kr * HQ * DK + 8 * ku) * (int)sizeof(TK);
+  auto kload = [&](Vec8<TK> &r, int c, int i) {
+    r.load(kt_rs, k_voff, (c * C + RPI * i) * HQ * DK * (int)sizeof(TK));
   };
-  Vec8<TK> kreg[KV8];
+  Vec8<TK> kreg[NKI];
 
   // PV role: channel group cg, key lane kl
   const int cg = tid % VCG, kl = tid / VCG;
@@ -132,9 +180,8 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(
 
   load_r(c_begin);
   if (s_role) {
-    const TK *kp = kptr(c_begin);
 #pragma unroll
-    for (int i = 0; i < KV8; ++i) kreg[i].load(kp + 8 * i);
+    for (int i = 0; i < NKI; ++i) kload(kreg[i], c_begin, i);
   }
 #pragma unroll
   for (int i = 0; i < KPL; ++i) vreg[i].load(vptr(c_begin, i));
@@ -150,22 +197,30 @@ __global__ __launch_bounds__(256, 3) void k_decode_split(
     load_r(cn);
     __syncthreads();
     if (s_role) {
-      const TK *kp = kptr(cn);
-      float s = 0.f;
+      const float4 qa = *reinterpret_cast<const float4 *>(&Qs[buf][sh][8 * ku]);
+      const float4 qb = *reinterpret_cast<const float4 *>(&Qs[buf][sh][8 * ku + 4]);
+      float part[NKI];
 #pragma unroll
-      for (int i = 0; i < KV8; ++i) {
-        const float4 qa = *reinterpret_cast<const float4 *>(&Qs[buf][sh][8 * i]);
-        const float4 qb = *reinterpret_cast<const float4 *>(&Qs[buf][sh][8 * i + 4]);
-        s = fmaf(qa.x, kreg[i][0], s);
-        s = fmaf(qa.y, kreg[i][1], s);
-        s = fmaf(qa.z, kreg[i][2], s);
-        s = fmaf(qa.w, kreg[i][3], s);
-        s = fmaf(qb.x, kreg[i][4], s);
-        s = fmaf(qb.y, kreg[i][5], s);
-        s = fmaf(qb.z, kreg[i][6], s);
-        s = fmaf(qb.w, kreg[i][7], s);
-        kreg[i].load(kp + 8 * i);  // same piece of the next chunk
+      for (int i = 0; i < NKI; ++i) {
+        float t = qa.x * kreg[i][0];
+        t = fmaf(qa.y, kreg[i][1], t);
+        t = fmaf(qa.z, kreg[i][2], t);
+        t = fmaf(qa.w, kreg[i][3], t);
+        t = fmaf(qb.x, kreg[i][4], t);
+        t = fmaf(qb.y, kreg[i][5], t);
+        t = fmaf(qb.z, kreg[i][6], t);
+        t = fmaf(qb.w, kreg[i][7], t);
+        part[i] = t;
+        kload(kreg[i], cn, i);  // same piece of the next chunk
       }
+      // sum each partial over the LPR lanes of its key row (rotations within
+      // a 16-lane row; for 8-lane rows the rotation by 8 is skipped and the
+      // two halves of a 16-lane row hold different keys)
+#pragma unroll
+      for (int i = 0; i < NKI; ++i) part[i] = row_sum<LPR>(part[i]);
+      float s = part[0];
+#pragma unroll
+      for (int i = 1; i < NKI; ++i) s = ku == i ? part[i] : s;
       if ((int64_t)c * C + kk >= T) s = -INFINITY;
       const float cm = wave_max(s);
       const float m_new = fmaxf(m_run, cm);  // finite: every chunk has a valid key

@@ -179,7 +179,9 @@ size_t wall_attn_decode_workspace_bytes(int64_t B, int64_t T_kv, int64_t HQ, int
  *   WA_F32) and r_cache as built above,
  *   sink_bias [HQ] float32 or NULL -> o [B,1,HQ,V] (dtype),
  *   lse [B,1,HQ] float32 natural log, or NULL.
- * Supported: chunk_size == 64, K and V in {64, 128}.
+ * Supported: chunk_size == 64, K and V in {64, 128}; T_kv*HQ*K times the
+ * k_tilde element size (2 or 4 bytes) < 2^31 (one batch row of the cache
+ * addressed with 32-bit offsets), else UNSUPPORTED.
  */
 int wall_attn_decode(const void *q, const void *v, const float *p_curr, const void *k_tilde,
                      const float *r_cache, const float *sink_bias, void *o, float *lse,
