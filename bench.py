@@ -2,7 +2,7 @@
 """Benchmark of libwallattn on one MI355X: Wall Attention prefill TFLOP/s at
 T = 8K and single-step decode GB/s over a 32K-token cache.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 100]
 
 One "step" is one call of wall_attn_fwd (running-sum pre-pass + attention)
 on the long-context workload B=1, T=8192, HQ=16, H=4, K=V=128, bf16, with
@@ -41,8 +41,11 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU needs some tens of milliseconds of work to reach steady clocks:
+    # with 5 warm-up steps (~2 ms) the first timed steps of the 8K prefill ran
+    # ~15% slower than later ones
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=1,
