@@ -36,6 +36,10 @@ class Prefill:
     len_lo: int = 0
     len_hi: int = 0
     seed: int = 0
+    # > 0: channel 0 of g is set to this rise in log2 units per token (times
+    # ln 2, as g is in nats) and channel 0 of k to zero, so the decay sum of
+    # that channel climbs steadily without adding to any score
+    rise_ch0_log2: float = 0.0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -121,6 +125,9 @@ def make_prefill(cfg: Prefill, device="cpu", seed: Optional[int] = None) -> dict
         gs = -torch.nn.functional.softplus(
             torch.randn(B, T, cfg.HQ, generator=gen, dtype=f32)) * cfg.g_scalar_std
     sink = torch.randn(cfg.HQ, generator=gen, dtype=f32) if cfg.sink else None
+    if cfg.rise_ch0_log2 > 0:
+        g[..., 0] = cfg.rise_ch0_log2 * 0.6931471805599453
+        k[..., 0] = 0.0
     dt = cfg.dtype
     out = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), g=g.to(dt),
                g_scalar=None if gs is None else gs.to(dt), sink_bias=sink,

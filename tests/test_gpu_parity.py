@@ -94,6 +94,14 @@ SMALL = [
     cfg("f32_T1", 1, 1, 2, 1, 64, 64, torch.float32, seed=20),
     cfg("bf16_T450_D128_gqa8_gate_sink_window300", 1, 450, 8, 1, 128, 128, torch.bfloat16,
         g_mode="neg_softplus", g_std=0.05, g_scalar_std=0.01, sink=True, window=300, seed=23),
+    # the decay sum of channel 0 rises 0.1 log2 units per token (that channel
+    # of k is zero): the second query tile's anchor lies ~13 log2 units above
+    # the first key chunk's, so the kernel rebalances that tile pair with
+    # sigma = 5 (query operand times 2^-5, scores times 2^5)
+    cfg("bf16_T256_rising_channel_sigma", 2, 256, 4, 2, 64, 64, torch.bfloat16,
+        rise_ch0_log2=0.1, g_scalar_std=0.01, sink=True, seed=24),
+    cfg("bf16_T256_D128_rising_channel_sigma_window100", 1, 256, 4, 1, 128, 128, torch.bfloat16,
+        rise_ch0_log2=0.1, window=100, seed=25),
 ]
 
 
