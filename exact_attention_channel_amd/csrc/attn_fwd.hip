@@ -169,8 +169,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   const int col = lane & 31, half = lane >> 5;
   const int hq = blockIdx.x % HQ;
   const int rest = blockIdx.x / HQ;
-  const int seg = rest % nseg;
-  const int I = NQT - 1 - rest / nseg;  // longest query tiles first
+  // Without a window, longest query tiles first over all segments (balance:
+  // a tile's key count grows with I).  With a window every tile sees about
+  // the same number of keys, so segments go one after the other and the
+  // workgroups running side by side are neighbouring query tiles of one
+  // sequence, sharing most of their key and value tiles in L2.
+  const int seg = window > 0 ? rest / NQT : rest % nseg;
+  const int I = NQT - 1 - (window > 0 ? rest % NQT : rest / nseg);
   int64_t bos64, eos64;
   segment_bounds(seg, T, cu, bos64, eos64);
   const int L = (int)(eos64 - bos64);  // sequence length; positions below are relative to bos
