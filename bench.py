@@ -212,9 +212,9 @@ def main():
             raise RuntimeError(lib.wall_attn_last_error().decode())
 
     def attend():
-        rc = lib.wall_attn_fwd_attend(ptr(x["v"]), ptr(x["g_scalar"]), ptr(x["sink_bias"]),
-                                      ptr(o), ptr(lse), B, T, HQ, H, K, V, None, 0, 0, 0,
-                                      wa.WA_BF16, ptr(ws), wsb, stream)
+        rc = lib.wall_attn_fwd_attend(ptr(x["q"]), ptr(x["v"]), ptr(x["g"]), ptr(x["g_scalar"]),
+                                      ptr(x["sink_bias"]), ptr(o), ptr(lse), B, T, HQ, H, K, V,
+                                      None, 0, 0, 0, scale, wa.WA_BF16, ptr(ws), wsb, stream)
         if rc:
             raise RuntimeError(lib.wall_attn_last_error().decode())
 

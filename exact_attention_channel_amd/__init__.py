@@ -62,7 +62,7 @@ def load_library():
     lib.wall_attn_fwd_prepare.restype = S
     lib.wall_attn_fwd_prepare.argtypes = [P, P, P, P, I, I, I, I, I, I, P, I, I, F, S, P, Z, P]
     lib.wall_attn_fwd_attend.restype = S
-    lib.wall_attn_fwd_attend.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, I, I, S, P, Z, P]
+    lib.wall_attn_fwd_attend.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, I, I, I, F, S, P, Z, P]
     lib.wall_attn_prefix_log2_workspace_bytes.restype = Z
     lib.wall_attn_prefix_log2_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.wall_attn_prefix_log2.restype = S

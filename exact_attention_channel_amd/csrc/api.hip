@@ -95,7 +95,8 @@ int fwd_impl(int stages, const char *name, const void *q, const void *k, const v
   if (rc != WA_OK) return rc;
   const bool need_inputs = (stages & STAGE_PREPARE) != 0;
   const bool need_outputs = (stages & STAGE_ATTEND) != 0;
-  if ((need_inputs && (!q || !k || !g)) || (need_outputs && (!v || !o)) || !workspace)
+  // the attention stage reads q and g as well (it forms the rescaled queries)
+  if ((need_inputs && (!q || !k || !g)) || (need_outputs && (!q || !g || !v || !o)) || !workspace)
     return fail(WA_INVALID_ARG, "%s: required pointers must be non-NULL", name);
   const void *ptrs[] = {q, k, v, g, g_scalar, sink_bias, o, lse, workspace};
   for (const void *ptr : ptrs)
@@ -141,14 +142,15 @@ int wall_attn_fwd_prepare(const void *q, const void *k, const void *g, const voi
                   dtype, workspace, workspace_bytes, stream);
 }
 
-int wall_attn_fwd_attend(const void *v, const void *g_scalar, const float *sink_bias, void *o,
-                         float *lse, int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K,
-                         int64_t V, const int32_t *cu_seqlens, int64_t num_seqs,
-                         int64_t max_seqlen, int64_t window_size, int dtype, void *workspace,
-                         size_t workspace_bytes, struct ihipStream_t *stream) {
-  return fwd_impl(STAGE_ATTEND, "wall_attn_fwd_attend", nullptr, nullptr, v, nullptr, g_scalar,
-                  sink_bias, o, lse, B, T, HQ, H, K, V, cu_seqlens, num_seqs, max_seqlen,
-                  window_size, 0.f, dtype, workspace, workspace_bytes, stream);
+int wall_attn_fwd_attend(const void *q, const void *v, const void *g, const void *g_scalar,
+                         const float *sink_bias, void *o, float *lse, int64_t B, int64_t T,
+                         int64_t HQ, int64_t H, int64_t K, int64_t V, const int32_t *cu_seqlens,
+                         int64_t num_seqs, int64_t max_seqlen, int64_t window_size, float scale,
+                         int dtype, void *workspace, size_t workspace_bytes,
+                         struct ihipStream_t *stream) {
+  return fwd_impl(STAGE_ATTEND, "wall_attn_fwd_attend", q, nullptr, v, g, g_scalar, sink_bias, o,
+                  lse, B, T, HQ, H, K, V, cu_seqlens, num_seqs, max_seqlen, window_size, scale,
+                  dtype, workspace, workspace_bytes, stream);
 }
 
 size_t wall_attn_prefix_log2_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t K,

@@ -138,11 +138,12 @@ __device__ __forceinline__ void vm_wait0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 template <int DK, int DV, bool HAS_GS>
 __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
-    const _Float16 *__restrict__ qh, const _Float16 *__restrict__ kt, const bf16_t *__restrict__ v,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ g, const float *__restrict__ off,
+    const _Float16 *__restrict__ kt, const bf16_t *__restrict__ v,
     const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ, int H, int nseg, int NCmax,
-    int NQT, int window) {
+    int NQT, int window, float qscale) {
   // Score product per 32-key tile and wave: S^T = K_tilde Q'^T over DK + 16
   // channels.  The key rows come from the pre-pass with their extra block
   // [1, 1, -Gs_j hi, -Gs_j lo, 0 ...]; the wave's query operand Q' holds
@@ -198,19 +199,6 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   const __amdgpu_buffer_rsrc_t kt_rs = make_rsrc(kt + ((int64_t)hq * ntok + bos64) * BT::KX, (int64_t)L * KRB);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v + (bos64 * H + h) * DV, (int64_t)L * vrow * 2);
 
-  // the wave's 32 rows of q_hat into LDS (read back once per anchor chunk)
-  {
-    constexpr int QP = DK / 8;  // 16-byte pieces per query row
-    const _Float16 *qh_b = qh + (bos64 * HQ + hq) * DK;
-#pragma unroll
-    for (int k = 0; k < 32 * QP / 64; ++k) {
-      const int g = lane + 64 * k, rr = g / QP, pc = g % QP;
-      const int r = qw0 + rr;
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (r < L) x = *reinterpret_cast<const u32x4 *>(qh_b + (int64_t)r * qrow + 8 * pc);
-      *reinterpret_cast<u32x4 *>(&Qs[(wv * 32 + rr) * QSB + 16 * pc]) = x;
-    }
-  }
   float g_i = 0.f;
   if (HAS_GS && qw0 + col < L) g_i = gsum[(bos64 + qw0 + col) * HQ + hq];
 
@@ -231,6 +219,60 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     rq[c] = anch_b[(int64_t)(2 * I) * HQ * DK + CPL * lane + c];  // query tile anchor
     araw[c] = 0.f;
   }
+
+  // q_hat of the wave's 32 rows into LDS (read back once per anchor chunk):
+  // the running decay sum of each channel is the chunk's offset plus the sum
+  // of g over the chunk's rows up to the row (the pre-pass forms the keys'
+  // the same way), and q_hat = q * 2^(P2 - RQ_I) * scale * log2(e).  Lane
+  // owns channels CPL*lane .. +CPL-1, so every row is one coalesced read.
+  // All of a wave's loads (g over the chunk up to its last row, q over its
+  // rows) go out together, one memory round trip, right after the first tile
+  // loads are issued.
+  auto make_qhat = [&]() {
+    if (!wave_live) return;
+    const int cw = qw0 / CHUNK, r0 = cw * CHUNK;  // the rows' chunk and its first row
+    const bool second = qw0 > r0;                 // the wave's rows are the chunk's second half
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = off[((cbase + cw) * HQ + hq) * DK + CPL * lane + c];
+    const bf16_t *g_b = g + (bos64 * HQ + hq) * DK + CPL * lane;
+    const bf16_t *q_b = q + (bos64 * HQ + hq) * DK + CPL * lane;
+    auto ld = [&](const bf16_t *base, int r) -> uint32_t {
+      if (r >= L) return 0u;
+      if (CPL == 2) return *reinterpret_cast<const uint32_t *>(base + (int64_t)r * qrow);
+      return base[(int64_t)r * qrow];
+    };
+    uint32_t gp[32], gw[32], qw[32];  // g of the chunk's first half (second-half waves), g and q of the rows
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      gp[u] = second ? ld(g_b, r0 + u) : 0u;
+      gw[u] = ld(g_b, qw0 + u);
+      qw[u] = ld(q_b, qw0 + u);
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      acc[0] += bf16_lo(gp[u]);
+      if (CPL == 2) acc[CPL - 1] += bf16_hi(gp[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 32; ++u) {
+      float qv[CPL];
+      acc[0] += bf16_lo(gw[u]);
+      qv[0] = bf16_lo(qw[u]);
+      if (CPL == 2) {
+        acc[CPL - 1] += bf16_hi(gw[u]);
+        qv[CPL - 1] = bf16_hi(qw[u]);
+      }
+      float qo[CPL];
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) qo[c] = qv[c] * fast_exp2(acc[c] * LOG2E - rq[c]) * qscale;
+      unsigned char *dst = &Qs[(wv * 32 + u) * QSB + 2 * CPL * lane];
+      if (CPL == 2)
+        *reinterpret_cast<uint32_t *>(dst) = pack_f16x2(qo[0], qo[CPL - 1]);
+      else
+        *reinterpret_cast<uint16_t *>(dst) = __builtin_bit_cast(uint16_t, (_Float16)qo[0]);
+    }
+  };
   auto load_a = [&](int chunk) {  // anchors of a key chunk, this lane's channels
     const int soff = chunk * HQ * DK * 4;
     if (CPL == 2) {
@@ -552,6 +594,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     dma_k(tileJ(0), K0);
     if (VAL) dma_v(tileJ(0), V0);
     if (1 < NTL) dma_k(tileJ(1), K1);
+    if (MODE == 0) make_qhat();  // overlaps the first tile loads
     float cs_cur = factors();
     rebuild();
     const bool nc1 = 1 < NTL && new_chunk(1);
@@ -811,11 +854,12 @@ hipError_t attn_bf16_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t 
   const int NQT = (int)((p.maxlen + QTILE - 1) / QTILE);
   const dim3 grid((unsigned)(NQT * p.nseg * p.HQ));
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(BfTile<DK, DV>::NTH), 0, st, static_cast<const _Float16 *>(ws.qh),
+    hipLaunchKernelGGL(kern, grid, dim3(BfTile<DK, DV>::NTH), 0, st,
+                       static_cast<const bf16_t *>(p.q), static_cast<const bf16_t *>(p.g), ws.csum,
                        static_cast<const _Float16 *>(ws.kt), static_cast<const bf16_t *>(p.v),
                        ws.anch, ws.gsum, p.sink, static_cast<bf16_t *>(p.o), p.lse, p.cu, p.T,
                        p.ntok, (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT,
-                       (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0));
+                       (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0), p.scale * LOG2E);
   };
   if (p.g_scalar != nullptr)
     args(k_attn_fwd_bf16<DK, DV, true>);

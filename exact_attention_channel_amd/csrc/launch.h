@@ -30,7 +30,7 @@ struct FwdWorkspace {
   float *csum;     // [nseg*NCmax, HQ, K] chunk sums of g, then exclusive chunk offsets
   float *anch;     // [nseg*NCmax, HQ, K] chunk anchors (log2 units)
   float *csum_s;   // [nseg*NCmax, HQ] chunk sums / offsets of g_scalar
-  void *qh;        // [ntok, HQ, K] rescaled queries (dtype)
+  void *qh;        // [ntok, HQ, K] rescaled queries (float operands only)
   void *kt;        // rescaled keys: bf16 path [HQ, ntok, K+16] half with extra
                    // channels, fp32 path [ntok, HQ, K] float
   float *gsum;     // [ntok, HQ] running gate sum (log2 units)

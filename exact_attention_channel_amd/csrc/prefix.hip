@@ -227,7 +227,10 @@ struct ChunkScan {
 // Phase C for the prefill: in-chunk running sums, then
 //   q_hat = q * 2^(P2 - RQ) * qscale   (RQ: anchor of the first chunk of the
 //                                       128-row query tile, so |P2 - RQ| is
-//                                       at most one chunk's decay span)
+//                                       at most one chunk's decay span;
+//                                       float operands only: for half
+//                                       operands the attention kernel forms
+//                                       q_hat from q, g and the chunk offsets)
 //   k_tilde = k * 2^(R_c - P2)         (R_c: anchor of this 64-token chunk)
 // written in the operand type (IEEE half for bf16 inputs, float for fp32).
 //   gsum = running sum of g_scalar in log2 units.
@@ -267,18 +270,21 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
     const int r = grp * CS::RPG + i;
     if (r < nrow) {
       const int64_t t = r0 + r;
-      const float4 qv = load4<TE>(q + (t * HQ + hq) * KD + 4 * q4);
+      if (!HM) {  // half operands: the attention kernel forms q_hat itself
+        const float4 qv = load4<TE>(q + (t * HQ + hq) * KD + 4 * q4);
+        float4 qo;
+        qo.x = qv.x * fast_exp2(p2[i].x - RQ.x) * qscale;
+        qo.y = qv.y * fast_exp2(p2[i].y - RQ.y) * qscale;
+        qo.z = qv.z * fast_exp2(p2[i].z - RQ.z) * qscale;
+        qo.w = qv.w * fast_exp2(p2[i].w - RQ.w) * qscale;
+        store4<TO>(qh + (t * HQ + hq) * KD + 4 * q4, qo);
+      }
       const float4 kv = load4<TE>(k + (t * H + h) * KD + 4 * q4);
-      float4 qo, ko;
-      qo.x = qv.x * fast_exp2(p2[i].x - RQ.x) * qscale;
-      qo.y = qv.y * fast_exp2(p2[i].y - RQ.y) * qscale;
-      qo.z = qv.z * fast_exp2(p2[i].z - RQ.z) * qscale;
-      qo.w = qv.w * fast_exp2(p2[i].w - RQ.w) * qscale;
+      float4 ko;
       ko.x = kv.x * fast_exp2(A.x - p2[i].x);
       ko.y = kv.y * fast_exp2(A.y - p2[i].y);
       ko.z = kv.z * fast_exp2(A.z - p2[i].z);
       ko.w = kv.w * fast_exp2(A.w - p2[i].w);
-      store4<TO>(qh + (t * HQ + hq) * KD + 4 * q4, qo);
       store4<TO>(kt + (HM ? (hq * ntok + t) : (t * HQ + hq)) * KX + 4 * q4, ko);
     }
   }
@@ -417,7 +423,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
   char *csum = take(sizeof(float) * nchunk * p.HQ * p.K);
   char *anch = take(sizeof(float) * nchunk * p.HQ * p.K);
   char *csum_s = take(sizeof(float) * nchunk * p.HQ);
-  char *qh = take(esz * p.ntok * p.HQ * p.K);
+  char *qh = take(p.dtype == 0 ? 0 : esz * p.ntok * p.HQ * p.K);  // bf16: q_hat formed in the attention kernel
   char *kt = take(esz * p.ntok * p.HQ * (p.dtype == 0 ? p.K + 16 : p.K));
   char *gsum = take(sizeof(float) * p.ntok * p.HQ);
   if (ws) {

@@ -106,14 +106,17 @@ int wall_attn_fwd(const void *q, const void *k, const void *v, const void *g,
  *
  * wall_attn_fwd_prepare: the running sums of g (and g_scalar) along each
  * sequence, the per-chunk anchors (README "Decode" and "Features": anchors
- * keep every exp2 argument bounded) and the rescaled operands, written into
- * `workspace`.  Reads q, k, g, g_scalar; arguments as in wall_attn_fwd.
+ * keep every exp2 argument bounded) and the rescaled keys (and, for WA_F32,
+ * the rescaled queries), written into `workspace`.  Reads q, k, g,
+ * g_scalar; arguments as in wall_attn_fwd.
  *
  * wall_attn_fwd_attend: the tiled causal attention over a prepared
  * workspace (README introduction: FlashAttention-style streaming softmax);
- * writes o and lse.  Reads v, sink_bias and the workspace.  g_scalar is not
- * read: pass non-NULL exactly when the workspace was prepared with a gate.
- * Shape arguments, cu_seqlens and dtype must equal those given to prepare;
+ * writes o and lse.  Reads q and g (for WA_BF16 each query tile's rescaled
+ * queries are formed here from q, g and the prepared chunk offsets), v,
+ * sink_bias and the workspace.  g_scalar is not read: pass non-NULL exactly
+ * when the workspace was prepared with a gate.  Shape arguments, q, g,
+ * scale, cu_seqlens and dtype must equal those given to prepare;
  * window_size may differ (it only selects keys).
  * Errors: as wall_attn_fwd.
  */
@@ -122,11 +125,12 @@ int wall_attn_fwd_prepare(const void *q, const void *k, const void *g, const voi
                           const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
                           float scale, int dtype, void *workspace, size_t workspace_bytes,
                           struct ihipStream_t *stream);
-int wall_attn_fwd_attend(const void *v, const void *g_scalar, const float *sink_bias, void *o,
-                         float *lse, int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K,
-                         int64_t V, const int32_t *cu_seqlens, int64_t num_seqs,
-                         int64_t max_seqlen, int64_t window_size, int dtype, void *workspace,
-                         size_t workspace_bytes, struct ihipStream_t *stream);
+int wall_attn_fwd_attend(const void *q, const void *v, const void *g, const void *g_scalar,
+                         const float *sink_bias, void *o, float *lse, int64_t B, int64_t T,
+                         int64_t HQ, int64_t H, int64_t K, int64_t V, const int32_t *cu_seqlens,
+                         int64_t num_seqs, int64_t max_seqlen, int64_t window_size, float scale,
+                         int dtype, void *workspace, size_t workspace_bytes,
+                         struct ihipStream_t *stream);
 
 /* Bytes of device workspace wall_attn_prefix_log2 needs (0 on bad arguments). */
 size_t wall_attn_prefix_log2_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t K,
