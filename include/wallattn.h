@@ -43,7 +43,7 @@ struct ihipStream_t; /* hipStream_t is `struct ihipStream_t *` */
 enum {
   WA_OK = 0,
   WA_INVALID_ARG = 1,        /* shapes, pointers or values that violate the contract */
-  WA_UNSUPPORTED = 2,        /* a valid request this build has no kernel for */
+  WA_UNSUPPORTED = 2,        /* a valid request the library has no kernel for */
   WA_HIP_ERROR = 3,          /* a HIP launch or query failed */
   WA_WORKSPACE_TOO_SMALL = 4 /* workspace_bytes below the matching *_workspace_bytes() */
 };
