@@ -212,7 +212,11 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   const int64_t cbase = (int64_t)seg * NCmax;
   const float *anch_b = anch + (cbase * HQ + hq) * DK;
   const int nch = (L + CHUNK - 1) / CHUNK;
-  const __amdgpu_buffer_rsrc_t an_rs = make_rsrc(anch_b, (int64_t)nch * HQ * DK * 4);
+  // built from explicitly uniform values: left to the compiler, the
+  // descriptor can land in vector registers and every anchor load becomes a
+  // loop over lanes
+  const __amdgpu_buffer_rsrc_t an_rs =
+      make_rsrc(anch + uniform64((cbase * HQ + hq) * DK), uniform64((int64_t)nch * HQ * DK * 4));
   float rq[CPL], araw[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
@@ -640,18 +644,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       const int kj0 = J * BK;
       const bool masked = kj0 + BK - 1 > qw0 || (window > 0 && qw0 + 31 - kj0 >= window);
       bf16x8 pB[2];
-      const bool general = masked || cs_cur != 1.f || (MODE == 0 && !all_set);
-      if (MODE != 1 && need_cur && need_next && !general) {
-        // steady state: one block of score MFMAs, exponentials and value
-        // MFMAs, with the next tiles' loads and the operand rebuild inside
-        const int Jk = t + 2 < NTL ? tileJ(t + 2) : 0;
-        // anchor chunks are two tiles long and start at even t unless a
-        // window or a short sequence shifts them: even iterations rebuild
-        // inside the block (always, the rebuild is idempotent), odd ones
-        // after it when their tile t+2 starts a chunk
-        fused(std::integral_constant<bool, P == 0>{}, Sc, Sn, Vc, Kn, Jk, Kc, Jn, Vn, t + 2 < NTL);
-        if (P == 1 && nc2) rebuild();
-      } else {
+      {
         if (t + 2 < NTL) dma_k(tileJ(t + 2), Kc);
         if (VAL && t + 1 < NTL) dma_v(Jn, Vn);
         if (need_next) {
@@ -681,10 +674,44 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       cs_next2 = cs3;
       vm_wait0();
     };
-    for (int t = 0; t < NTL; t += 2) {
-      body(std::integral_constant<int, 0>{}, t, Sa, Sb);
-      if (t + 1 >= NTL) break;
-      body(std::integral_constant<int, 1>{}, t + 1, Sb, Sa);
+    // A pair of tiles t (even, the first of an anchor chunk) and t + 1, both
+    // older than the query tile's own key tiles, outside the window edge,
+    // with every row's reference set and sigma = 0 for their chunk, with
+    // tiles up to t + 4 still to come: body() would take its steady-state
+    // block for both, rebuild inside the first one and publish the factors
+    // of chunk(t + 4) after the second one.  The same work with every
+    // condition known in advance.
+    auto pair_ok = [&](int t) -> bool {
+      if (MODE == 1 || t < ND || t + 2 >= NTL) return false;
+      const int J = tileJ(t);
+      if ((J & 1) || (window > 0 && qw0 + 31 - J * BK >= window)) return false;
+      return __ballot(!(all_set && cs_cur == 1.f && cs_next == 1.f)) == 0;
+    };
+    auto steady_pair = [&](int t) {
+      const int J = tileJ(t);  // tiles t .. t + 3 are J .. J + 3
+      __syncthreads();
+      fused(std::true_type{}, Sa, Sb, V0, K1, J + 2, K0, J + 1, V1, true);
+      cs_cur = cs_next;
+      cs_next = cs_next2;
+      vm_wait0();
+      __syncthreads();
+      const bool nc4 = t + 4 < NTL;  // tile t + 4 exists (and starts a chunk)
+      if (nc4) load_a((J + 4) >> 1);
+      fused(std::false_type{}, Sb, Sa, V1, K0, J + 3, K1, J + 2, V0, t + 3 < NTL);
+      float cs3 = cs_next2;
+      if (nc4) cs3 = factors();
+      cs_cur = cs_next;
+      cs_next = cs_next2;
+      cs_next2 = cs3;
+      vm_wait0();
+    };
+    int t = 0;
+    while (t < NTL) {
+      for (; t < NTL && !pair_ok(t); t += 2) {
+        body(std::integral_constant<int, 0>{}, t, Sa, Sb);
+        if (t + 1 < NTL) body(std::integral_constant<int, 1>{}, t + 1, Sb, Sa);
+      }
+      for (; t < NTL && pair_ok(t); t += 2) steady_pair(t);
     }
   };
   auto reset = [&](bool known) {
