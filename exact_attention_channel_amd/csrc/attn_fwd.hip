@@ -398,6 +398,18 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     const f16x8 a = *reinterpret_cast<const f16x8 *>(Kb + sa_off + ks * 32);
     S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qB[ks], S, 0, 0, 0);
   };
+  // k-steps 0 .. n-1 of a tile's scores into a fresh accumulator, every
+  // operand read issued before the first MFMA (one LDS round trip, not n)
+  auto s_batch = [&](auto n_c, f32x16 &S, const unsigned char *Kb) {
+    constexpr int N = decltype(n_c)::value;
+    f16x8 a[N];
+#pragma unroll
+    for (int ks = 0; ks < N; ++ks) a[ks] = *reinterpret_cast<const f16x8 *>(Kb + sa_off + ks * 32);
+    __builtin_amdgcn_sched_barrier(0);
+    S = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < N; ++ks) S = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qB[ks], S, 0, 0, 0);
+  };
   // The S^T accumulator holds, in lane (col, half), keys 8 (r/4) + 4 half + r%4
   // (r = 0..15) of query column col.  Its elements r = 8t..8t+7 are directly
   // the B operand (k = 16 keys) of the value product, with the keys in the
@@ -413,12 +425,20 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     const s16x4 a0 = lds_read_tr4(base), a1 = lds_read_tr4(base + 8 * VRB);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto pv = [&](const unsigned char *Vb, const bf16x8 (&pB)[2]) {
+  // value operands of a whole tile, read ahead of the softmax that feeds them
+  auto vload = [&](const unsigned char *Vb, bf16x8 (&va)[2 * NMB]) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) va[2 * mb + s] = vread8(Vb, mb, s);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto pv = [&](const bf16x8 (&va)[2 * NMB], const bf16x8 (&pB)[2]) {
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vread8(Vb, mb, s), pB[s], oacc[mb], 0, 0, 0);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[2 * mb + s], pB[s], oacc[mb], 0, 0, 0);
   };
   auto mask = [&](f32x16 &S, int kj0) {
     const int rel = qw0 + col - kj0 - 4 * half;  // allowed: kk <= rel
@@ -614,11 +634,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     f32x16 Sa, Sb;
     {
       const int J = tileJ(0);
-      if (J >= Jlo_w && J <= Jhi_w) {
-        Sa = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s_mfma(Sa, K0, ks);
-      }
+      if (J >= Jlo_w && J <= Jhi_w) s_batch(std::integral_constant<int, NKS>{}, Sa, K0);
     }
     if (nc1) rebuild();
     float cs_next2 = cs_next;  // 2^sigma of the tile after next
@@ -647,13 +663,11 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       {
         if (t + 2 < NTL) dma_k(tileJ(t + 2), Kc);
         if (VAL && t + 1 < NTL) dma_v(Jn, Vn);
-        if (need_next) {
-          Sn = f32x16{};
-#pragma unroll
-          for (int ks = 0; ks < NKS - 1; ++ks) s_mfma(Sn, Kn, ks);
-        }
+        if (need_next) s_batch(std::integral_constant<int, NKS - 1>{}, Sn, Kn);
         if (need_cur) {
           __asm__ volatile("s_nop 0");  // keep this a branch
+          bf16x8 va[2 * NMB];
+          if (VAL) vload(Vc, va);
           if (masked) mask(Sc, kj0);
           if (cs_cur != 1.f) Sc *= cs_cur;
           if (MODE == 1) {
@@ -661,7 +675,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
           } else {
             if (MODE == 0 && !all_set) set_rows(Sc);
             tail(Sc, pB);
-            pv(Vc, pB);
+            pv(va, pB);
           }
         }
         if (need_next) s_mfma(Sn, Kn, NKS - 1);  // after any change of the row reference
