@@ -49,7 +49,7 @@ int check_fwd_shape(int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int6
   const int64_t nseg = varlen ? num_seqs : B;
   const int64_t maxlen = varlen ? max_seqlen : T;
   const int64_t ntok = varlen ? T : B * T;
-  if (nseg > 65535 || HQ > 65535 || (maxlen + 63) / 64 > (int64_t)1 << 30)
+  if (nseg > 65535 || HQ > 65535 || ((maxlen + 63) / 64 + 8) * HQ * nseg >= (int64_t)1 << 31)
     return fail(WA_UNSUPPORTED, "problem too large for the launch grid");
   // the bf16 attention kernel addresses one sequence's queries, values and
   // gate sums (token-major) and one head's rescaled keys (K+16 channels per
@@ -190,7 +190,7 @@ int wall_attn_build_kv_cache(const void *k, const float *P2, void *k_tilde, floa
   if (!k || !P2 || !k_tilde || !r_cache) return fail(WA_INVALID_ARG, "k, P2, k_tilde and r_cache must be non-NULL");
   if (!aligned16(k) || !aligned16(P2) || !aligned16(k_tilde) || !aligned16(r_cache))
     return fail(WA_INVALID_ARG, "device pointers must be 16-byte aligned");
-  if ((T_kv + 63) / 64 > 2147483647LL || B > 65535) return fail(WA_UNSUPPORTED, "problem too large for the launch grid");
+  if (((T_kv + 63) / 64 + 8) * HQ > 2147483647LL || B > 65535) return fail(WA_UNSUPPORTED, "problem too large for the launch grid");
   hipError_t e = wa::launch_build_cache(k, P2, k_tilde, r_cache, B, T_kv, HQ, H, K, dtype,
                                         reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(WA_HIP_ERROR, "wall_attn_build_kv_cache launch failed: %s", hipGetErrorString(e));

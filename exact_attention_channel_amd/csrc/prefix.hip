@@ -55,6 +55,38 @@ __device__ __forceinline__ void store4<float>(float *p, float4 x) {
   *reinterpret_cast<float4 *>(p) = x;
 }
 
+// Workgroup x of a per-(chunk, query head) grid -> (hq, c); false for the
+// padding workgroups.  Two orders, chosen on the host by grid size:
+//  * chunk order (c fastest): for a grid the GPU holds at once; whole chunks
+//    of every head then share an XCD (workgroups go to the 8 XCDs round
+//    robin), which measured fastest for one 8K-token sequence;
+//  * pair order: pairs p = (key/value head h, chunk c) with h fastest, the
+//    G query heads of a pair on one XCD (they read the pair's key rows
+//    through one L2), so that a grid that runs in many waves keeps the rows
+//    in flight together (16 packed sequences: phase C 222 -> 194 us).
+struct ChunkGrid {
+  int H, G, NC, pair;
+  __device__ __forceinline__ bool map(int x, int &hq, int &c) const {
+    if (!pair) {
+      c = x % NC;
+      hq = x / NC;
+      return true;
+    }
+    const int r = x >> 3, g = r % G, pr = 8 * (r / G) + (x & 7);
+    c = pr / H;
+    hq = (pr % H) * G + g;
+    return c < NC;
+  }
+  unsigned size() const {
+    return (unsigned)(pair ? 8 * (int64_t)G * (((int64_t)H * NC + 7) / 8) : (int64_t)H * G * NC);
+  }
+};
+// nrep: the grid's second dimension (segments or batch rows)
+inline ChunkGrid chunk_grid(int64_t H, int64_t G, int64_t NC, int64_t nrep) {
+  constexpr int64_t RESIDENT = 256 * 8;  // 256-thread workgroups the GPU holds at once
+  return ChunkGrid{(int)H, (int)G, (int)NC, H * G * NC * nrep > 2 * RESIDENT ? 1 : 0};
+}
+
 __device__ __forceinline__ float wave_inclusive_scan(float x) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -66,15 +98,17 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
 }
 
 // Phase A: sum of g (per channel) and of g_scalar over each chunk.
-// grid (NCmax, HQ, nseg), 256 threads; a thread owns 4 channels.
+// grid (cg.size(), nseg), 256 threads; a thread owns 4 channels.
 template <typename TE, int KD>
 __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
                                                     const TE *__restrict__ gs,
                                                     float *__restrict__ csum,
                                                     float *__restrict__ csum_s,
                                                     const int32_t *__restrict__ cu, int64_t T,
-                                                    int HQ, int NCmax) {
-  const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
+                                                    int HQ, int NCmax, ChunkGrid cg) {
+  int hq, c;
+  if (!cg.map(blockIdx.x, hq, c)) return;
+  const int s = blockIdx.y;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
   const int64_t r0 = bos + (int64_t)c * CHUNK;
@@ -239,17 +273,19 @@ struct ChunkScan {
 // gsum of the token split into two halves, 0 without a gate), so a key tile
 // is one contiguous block and the attention kernel's score product also
 // subtracts the row shift and the gate.  Float operands keep [ntok, HQ, KD].
-// grid (NCmax, HQ, nseg), 256 threads; a thread owns 4 channels.
+// grid (cg.size(), nseg), 256 threads; a thread owns 4 channels.
 template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
 __global__ __launch_bounds__(256) void k_prefill_operands(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ g,
     const TE *__restrict__ gs, const float *__restrict__ off, const float *__restrict__ anch,
     const float *__restrict__ off_s, TO *__restrict__ qh, TO *__restrict__ kt,
     float *__restrict__ gsum, const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ,
-    int H, int NCmax, float qscale) {
+    int H, int NCmax, float qscale, ChunkGrid cg) {
   constexpr bool HM = std::is_same<TO, _Float16>::value;  // head-major rows with extras
   constexpr int KX = HM ? KD + 16 : KD;
-  const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
+  int hq, c;
+  if (!cg.map(blockIdx.x, hq, c)) return;
+  const int s = blockIdx.y;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
   const int64_t r0 = bos + (int64_t)c * CHUNK;
@@ -313,8 +349,10 @@ __global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
                                                       const float *__restrict__ off,
                                                       float *__restrict__ P2,
                                                       const int32_t *__restrict__ cu, int64_t T,
-                                                      int HQ, int NCmax) {
-  const int c = blockIdx.x, hq = blockIdx.y, s = blockIdx.z;
+                                                      int HQ, int NCmax, ChunkGrid cg) {
+  int hq, c;
+  if (!cg.map(blockIdx.x, hq, c)) return;
+  const int s = blockIdx.y;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
   const int64_t r0 = bos + (int64_t)c * CHUNK;
@@ -334,14 +372,16 @@ __global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
 }
 
 // Decode cache: r_cache[c] = P2 at the chunk's last token (copied), and
-// k_tilde = k * 2^(r_cache[c] - P2) in the operand type.  grid (NC, HQ, B),
-// 256 threads; each thread owns 4 channels.
+// k_tilde = k * 2^(r_cache[c] - P2) in the operand type.
+// grid (cg.size(), B), 256 threads; each thread owns 4 channels.
 template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
 __global__ __launch_bounds__(256) void k_build_cache(const TE *__restrict__ k,
                                                      const float *__restrict__ P2,
                                                      TO *__restrict__ kt, float *__restrict__ rc,
-                                                     int64_t T, int HQ, int H, int NC) {
-  const int c = blockIdx.x, hq = blockIdx.y, b = blockIdx.z;
+                                                     int64_t T, int HQ, int H, int NC, ChunkGrid cg) {
+  int hq, c;
+  if (!cg.map(blockIdx.x, hq, c)) return;
+  const int b = blockIdx.y;
   const int64_t r0 = (int64_t)c * CHUNK;
   const int nrow = (T - r0) < CHUNK ? (int)(T - r0) : CHUNK;
   const int h = hq / (HQ / H);
@@ -370,20 +410,21 @@ template <typename TE, int KD>
 hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
   typedef typename OperandOf<TE>::type TO;
   const int NCmax = (int)((p.maxlen + CHUNK - 1) / CHUNK);
-  const dim3 gridA(NCmax, (unsigned)p.HQ, (unsigned)p.nseg);
+  const ChunkGrid cgA = chunk_grid(p.HQ, 1, NCmax, p.nseg), cgC = chunk_grid(p.H, p.HQ / p.H, NCmax, p.nseg);
+  const dim3 gridA(cgA.size(), (unsigned)p.nseg), gridC(cgC.size(), (unsigned)p.nseg);
   const TE *gs = static_cast<const TE *>(p.g_scalar);
   hipLaunchKernelGGL((k_chunk_sums<TE, KD>), gridA, dim3(256), 0, st,
                      static_cast<const TE *>(p.g), gs, ws.csum, ws.csum_s, p.cu, p.T, (int)p.HQ,
-                     NCmax);
+                     NCmax, cgA);
   const dim3 gridB((unsigned)p.HQ, (unsigned)p.nseg, (KD + 1 + 31) / 32);
   hipLaunchKernelGGL((k_chunk_scan<KD>), gridB, dim3(256), 0, st, ws.csum, ws.anch, ws.csum_s,
                      p.cu, p.T, (int)p.HQ, NCmax, gs != nullptr ? 1 : 0);
   const float qscale = p.scale * LOG2E;
-  hipLaunchKernelGGL((k_prefill_operands<TE, KD>), gridA, dim3(256), 0, st,
+  hipLaunchKernelGGL((k_prefill_operands<TE, KD>), gridC, dim3(256), 0, st,
                      static_cast<const TE *>(p.q), static_cast<const TE *>(p.k),
                      static_cast<const TE *>(p.g), gs, ws.csum, ws.anch, ws.csum_s,
                      static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt), ws.gsum, p.cu, p.T,
-                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale);
+                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC);
   return hipGetLastError();
 }
 
@@ -391,10 +432,11 @@ template <typename TE, int KD>
 hipError_t prefix_log2_t(const void *g, float *P2, const int32_t *cu, int64_t T, int64_t HQ,
                          int64_t nseg, int64_t maxlen, float *csum, hipStream_t st) {
   const int NCmax = (int)((maxlen + CHUNK - 1) / CHUNK);
-  const dim3 gridA(NCmax, (unsigned)HQ, (unsigned)nseg);
+  const ChunkGrid cgA = chunk_grid(HQ, 1, NCmax, nseg);
+  const dim3 gridA(cgA.size(), (unsigned)nseg);
   hipLaunchKernelGGL((k_chunk_sums<TE, KD>), gridA, dim3(256), 0, st,
                      static_cast<const TE *>(g), (const TE *)nullptr, csum, (float *)nullptr, cu,
-                     T, (int)HQ, NCmax);
+                     T, (int)HQ, NCmax, cgA);
   // The anchors of phase B are not needed here; they go to the upper half of
   // the workspace, which prefix_workspace_layout reserves for them.
   float *anch = csum + (int64_t)nseg * NCmax * HQ * KD;
@@ -402,7 +444,7 @@ hipError_t prefix_log2_t(const void *g, float *P2, const int32_t *cu, int64_t T,
   hipLaunchKernelGGL((k_chunk_scan<KD>), gridB, dim3(256), 0, st, csum, anch, (float *)nullptr,
                      cu, T, (int)HQ, NCmax, 0);
   hipLaunchKernelGGL((k_prefix_write<TE, KD>), gridA, dim3(256), 0, st,
-                     static_cast<const TE *>(g), csum, P2, cu, T, (int)HQ, NCmax);
+                     static_cast<const TE *>(g), csum, P2, cu, T, (int)HQ, NCmax, cgA);
   return hipGetLastError();
 }
 
@@ -465,25 +507,26 @@ hipError_t launch_build_cache(const void *k, const float *P2, void *kt, float *r
                               int64_t T, int64_t HQ, int64_t H, int64_t K, int dtype,
                               hipStream_t st) {
   const int NC = (int)((T + CHUNK - 1) / CHUNK);
-  const dim3 grid(NC, (unsigned)HQ, (unsigned)B);
+  const ChunkGrid cg = chunk_grid(H, HQ / H, NC, B);
+  const dim3 grid(cg.size(), (unsigned)B);
   if (dtype == 0) {
     if (K == 64)
       hipLaunchKernelGGL((k_build_cache<bf16_t, 64>), grid, dim3(256), 0, st,
                          static_cast<const bf16_t *>(k), P2, static_cast<_Float16 *>(kt), rc, T,
-                         (int)HQ, (int)H, NC);
+                         (int)HQ, (int)H, NC, cg);
     else
       hipLaunchKernelGGL((k_build_cache<bf16_t, 128>), grid, dim3(256), 0, st,
                          static_cast<const bf16_t *>(k), P2, static_cast<_Float16 *>(kt), rc, T,
-                         (int)HQ, (int)H, NC);
+                         (int)HQ, (int)H, NC, cg);
   } else {
     if (K == 64)
       hipLaunchKernelGGL((k_build_cache<float, 64>), grid, dim3(256), 0, st,
                          static_cast<const float *>(k), P2, static_cast<float *>(kt), rc, T,
-                         (int)HQ, (int)H, NC);
+                         (int)HQ, (int)H, NC, cg);
     else
       hipLaunchKernelGGL((k_build_cache<float, 128>), grid, dim3(256), 0, st,
                          static_cast<const float *>(k), P2, static_cast<float *>(kt), rc, T,
-                         (int)HQ, (int)H, NC);
+                         (int)HQ, (int)H, NC, cg);
   }
   return hipGetLastError();
 }
