@@ -381,6 +381,10 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   };
   // the wave's d-th load of an iteration: key loads first, then value loads
   constexpr int NDM = NKM + NVM;
+  // a tile of 9 (or 5) KiB leaves a last load for the first wave(s) only;
+  // the steady-state block issues that one right at its start, so that the
+  // block itself has no branch on the wave index
+  constexpr int KR = (BT::NKI % NWV) ? NKM - 1 : -1, VR = (BT::NVI % NWV) ? NVM - 1 : -1;
   auto dma_one = [&](int d, int Jk, unsigned char *kbuf, int Jv, unsigned char *vbuf, bool kdo, bool vdo) {
     if (d < NKM) {
       const int i = wv + NWV * d;
@@ -528,6 +532,8 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
         fr[ks] = f_read(ks);
       }
     };
+    if (KR >= 0 && kdo && wv + NWV * KR < BT::NKI) dma16(kt_rs, kbuf + 1024 * (wv + NWV * KR), koff[KR], Jk * BK * KRB);
+    if (VR >= 0 && wv + NWV * VR < BT::NVI) dma16(v_rs, vbuf + 1024 * (wv + NWV * VR), voff[VR], Jv * BK * vrow * 2);
     float pr[16];
     bf16x8 pb[2];
     float rs[2] = {0.f, 0.f};
@@ -556,7 +562,8 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
         const int j = FO.idx[n], mb = j % NMB, st = j / NMB;
         oacc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[j], pb[st], oacc[mb], 0, 0, 0);
       }
-      if (n >= DSLOT && n - DSLOT < NDM) dma_one(n - DSLOT, Jk, kbuf, Jv, vbuf, kdo, true);
+      if (n >= DSLOT && n - DSLOT < NDM && n - DSLOT != KR && n - DSLOT != NKM + VR)
+        dma_one(n - DSLOT, Jk, kbuf, Jv, vbuf, kdo, true);
       if (n < FO.S_ALONE) {
         const int e0 = n * E / FO.S_ALONE, e1 = (n + 1) * E / FO.S_ALONE;
 #pragma unroll
