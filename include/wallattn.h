@@ -89,7 +89,9 @@ size_t wall_attn_fwd_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t H
  * addressed with 32-bit offsets).
  * Errors: INVALID_ARG for HQ % H != 0,
  * cu_seqlens with B != 1, non-positive sizes, NULL required pointers or
- * misaligned pointers; UNSUPPORTED for other K, V or dtype;
+ * misaligned pointers; UNSUPPORTED for other K, V or dtype, and for a launch
+ * grid beyond the hardware's (segments or HQ above 65535, or
+ * HQ*(ceil(max_seqlen/64)+8)*segments >= 2^31, segments = num_seqs or B);
  * WORKSPACE_TOO_SMALL; HIP_ERROR if a launch fails.
  */
 int wall_attn_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -159,7 +161,8 @@ int wall_attn_prefix_log2(const void *g, float *P2, int64_t B, int64_t T, int64_
  *      inputs (same size as bfloat16 with 3 more mantissa bits; every stored
  *      factor 2^(R_c - P2[j]) spans at most one chunk's decay), float32 for
  *      WA_F32;  r_cache [B,ceil(T_kv/C),HQ,K] float32.
- * Supported: chunk_size == 64, K in {64, 128}.
+ * Supported: chunk_size == 64, K in {64, 128}; B <= 65535 and
+ * HQ*(ceil(T_kv/64)+8) < 2^31 (launch grid), else UNSUPPORTED.
  */
 int wall_attn_build_kv_cache(const void *k, const float *P2, void *k_tilde, float *r_cache,
                              int64_t B, int64_t T_kv, int64_t HQ, int64_t H, int64_t K,
