@@ -162,7 +162,9 @@ int wall_attn_prefix_log2(const void *g, float *P2, int64_t B, int64_t T, int64_
  *      factor 2^(R_c - P2[j]) spans at most one chunk's decay), float32 for
  *      WA_F32;  r_cache [B,ceil(T_kv/C),HQ,K] float32.
  * Supported: chunk_size == 64, K in {64, 128}; B <= 65535 and
- * HQ*(ceil(T_kv/64)+8) < 2^31 (launch grid), else UNSUPPORTED.
+ * HQ*(ceil(T_kv/64)+8)*B < 2^31 (launch grid); for WA_BF16 also
+ * T_kv*HQ*K*2 < 2^31 (the forward's per-sequence limit, which the decode
+ * shares); else UNSUPPORTED.
  */
 int wall_attn_build_kv_cache(const void *k, const float *P2, void *k_tilde, float *r_cache,
                              int64_t B, int64_t T_kv, int64_t HQ, int64_t H, int64_t K,
