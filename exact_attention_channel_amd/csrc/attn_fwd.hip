@@ -185,7 +185,10 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   const int h = hq / (HQ / H);
   const int i0 = I * QTILE;
   const int i_last = min(i0 + QTILE, L) - 1;
-  const int Jlo = (window > 0 ? max(0, i0 - window + 1) : 0) / BK;
+  // rounded down to the start of an anchor chunk, so that the older tiles
+  // pair up with chunks (see the steady pairs below); the tile this may add
+  // lies below every row's window, and each wave skips it
+  const int Jlo = ((window > 0 ? max(0, i0 - window + 1) : 0) / BK) & ~1;
   const int Jhi = i_last / BK;
 
   // this wave's rows qw0 .. qw0 + 31 and the key tiles they see
