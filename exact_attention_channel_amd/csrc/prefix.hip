@@ -185,16 +185,29 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
     stride = HQ;
   }
   // the chunk sums are read in batches of 8 independent loads: one memory
-  // round trip per batch instead of one per chunk
+  // round trip per batch instead of one per chunk; up to MAXS chunks per
+  // thread (sequences up to 8192 tokens) stay in registers for the second
+  // pass, so the whole scan is one round trip
+  constexpr int MAXS = 16;
+  const bool in_regs = span <= MAXS;
+  float xs[MAXS];
   float tot = 0.f;
-  if (active)
-    for (int c = cb; c < ce; c += 8) {
-      float x[8];
+  if (active) {
+    if (in_regs) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? p[(int64_t)(c + u) * stride] : 0.f;
+      for (int u = 0; u < MAXS; ++u) xs[u] = cb + u < ce ? p[(int64_t)(cb + u) * stride] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) tot += x[u];
+      for (int u = 0; u < MAXS; ++u) tot += xs[u];
+    } else {
+      for (int c = cb; c < ce; c += 8) {
+        float x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? p[(int64_t)(c + u) * stride] : 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) tot += x[u];
+      }
     }
+  }
   __shared__ float part[8][32];
   part[grp][threadIdx.x & 31] = tot;
   __syncthreads();
@@ -202,6 +215,17 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
   float run = 0.f;
   for (int q = 0; q < grp; ++q) run += part[q][threadIdx.x & 31];
   float *a = anch + (c0 * HQ + hq) * KD + ch;
+  if (in_regs) {
+#pragma unroll
+    for (int u = 0; u < MAXS; ++u) {
+      if (cb + u < ce) {
+        p[(int64_t)(cb + u) * stride] = run;
+        if (ch < KD) a[(int64_t)(cb + u) * stride] = rintf((run + xs[u]) * LOG2E);
+      }
+      run += xs[u];
+    }
+    return;
+  }
   for (int c = cb; c < ce; c += 8) {
     float x[8];
 #pragma unroll
