@@ -102,6 +102,11 @@ SMALL = [
         rise_ch0_log2=0.1, g_scalar_std=0.01, sink=True, seed=24),
     cfg("bf16_T256_D128_rising_channel_sigma_window100", 1, 256, 4, 1, 128, 128, torch.bfloat16,
         rise_ch0_log2=0.1, window=100, seed=25),
+    # 64 packed sequences x 8 heads x up to 11 chunks: more pre-pass
+    # workgroups than the GPU holds at once, so the pre-pass runs its
+    # (key/value head, chunk) pair order
+    cfg("bf16_varlen64_gqa4_pair_order", 1, 0, 8, 2, 64, 64, torch.bfloat16, nseq=64, len_lo=1,
+        len_hi=700, g_scalar_std=0.01, sink=True, seed=26),
 ]
 
 
@@ -325,9 +330,12 @@ def test_prefix_log2_matches_oracle(wa):
     check(P2, oracle.prefix_log2(y["g"], cu_seqlens=y["cu_seqlens"]), 1e-4, "prefix_log2 varlen")
 
 
+@pytest.mark.parametrize("B,T", [(3, 300), (32, 1100)], ids=["chunk_order", "pair_order"])
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_build_cache_matches_oracle(wa, dtype):
-    x = small_decode(T=300, dtype=dtype)
+def test_build_cache_matches_oracle(wa, dtype, B, T):
+    # 32 x 18 chunks x 8 heads exceed the workgroups the GPU holds at once:
+    # the cache build then runs its (key/value head, chunk) pair order
+    x = small_decode(B=B, T=T, dtype=dtype)
     P2 = torch.from_numpy(oracle.prefix_log2(x["g"]).astype(np.float32))
     kt, rc = wa.build_wall_kv_cache(x["k"].to(DEV), P2.to(DEV), chunk_size=64)
     rkt, rrc = oracle.build_kv_cache(x["k"], P2, chunk_size=64)
