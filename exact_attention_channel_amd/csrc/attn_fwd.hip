@@ -512,10 +512,11 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   // its MFMA-dense part at raised priority so that the other wave on the SIMD
   // fills the gaps with its own VALU and LDS work.
   // The block also issues the wave's LDS-direct loads of the next tiles (one
-  // per slot from slot DSLOT on) and, with RB, rebuilds each k-step of the
-  // query operand for the tile after next right after the score MFMA that
-  // last reads it, from the factors last published (the same values again
-  // when that tile's chunk is not new, so no branch is needed in the block).
+  // per slot from slot DSLOT on; a tile's ragged last load just before the
+  // block) and, with RB, rebuilds each k-step of the query operand for the
+  // tile after next right after the score MFMA that last reads it, from the
+  // factors last published (the first block of a steady pair, whose tile
+  // after next starts a chunk).
   auto fused = [&](auto rb_c, f32x16 &Sc, f32x16 &Sn, const unsigned char *Vb, const unsigned char *Kb,
                    int Jk, unsigned char *kbuf, int Jv, unsigned char *vbuf, bool kdo) {
     constexpr bool RB = decltype(rb_c)::value;
