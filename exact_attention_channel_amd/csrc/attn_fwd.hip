@@ -568,8 +568,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       }
       if (n >= DSLOT && n - DSLOT < NDM && n - DSLOT != KR && n - DSLOT != NKM + VR)
         dma_one(n - DSLOT, Jk, kbuf, Jv, vbuf, kdo, true);
-      if (n < FO.S_ALONE) {
-        const int e0 = n * E / FO.S_ALONE, e1 = (n + 1) * E / FO.S_ALONE;
+      // exponentials: the first half (probabilities of the first 16-key
+      // step) in the score-only slots, the second half spread over the slots
+      // up to the first value MFMA that needs them
+      constexpr int XS = FO.slot_p[NMB] - FO.S_ALONE;
+      if (n < FO.S_ALONE + XS) {
+        const int e0 = n < FO.S_ALONE ? n * (E / 2) / FO.S_ALONE : E / 2 + (n - FO.S_ALONE) * (E / 2) / XS;
+        const int e1 = n < FO.S_ALONE ? (n + 1) * (E / 2) / FO.S_ALONE : E / 2 + (n - FO.S_ALONE + 1) * (E / 2) / XS;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           if (e < e0 || e >= e1) continue;
