@@ -55,6 +55,52 @@ __device__ __forceinline__ void store4<float>(float *p, float4 x) {
   *reinterpret_cast<float4 *>(p) = x;
 }
 
+// N consecutive channels as floats; the pre-pass moves 16 bytes of its input
+// type per access (CPT = 8 bfloat16 or 4 float channels per thread).
+template <typename TE> constexpr int cpt() { return 16 / (int)sizeof(TE); }
+template <int N> struct FV {
+  float v[N];
+};
+template <int N> __device__ __forceinline__ FV<N> zerov() {
+  FV<N> r;
+#pragma unroll
+  for (int j = 0; j < N; ++j) r.v[j] = 0.f;
+  return r;
+}
+template <typename TE, int N> __device__ __forceinline__ FV<N> loadv(const TE *p);
+template <> __device__ __forceinline__ FV<8> loadv<bf16_t, 8>(const bf16_t *p) {
+  const u32x4 w = *reinterpret_cast<const u32x4 *>(p);
+  FV<8> r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r.v[2 * j] = bf16_lo(w[j]);
+    r.v[2 * j + 1] = bf16_hi(w[j]);
+  }
+  return r;
+}
+template <> __device__ __forceinline__ FV<4> loadv<float, 4>(const float *p) {
+  const float4 x = *reinterpret_cast<const float4 *>(p);
+  return FV<4>{{x.x, x.y, x.z, x.w}};
+}
+template <> __device__ __forceinline__ FV<8> loadv<float, 8>(const float *p) {
+  const float4 x = reinterpret_cast<const float4 *>(p)[0], y = reinterpret_cast<const float4 *>(p)[1];
+  return FV<8>{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
+}
+template <typename TO, int N> __device__ __forceinline__ void storev(TO *p, const FV<N> &x);
+template <> __device__ __forceinline__ void storev<_Float16, 8>(_Float16 *p, const FV<8> &x) {
+  u32x4 w;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = pack_f16x2(x.v[2 * j], x.v[2 * j + 1]);
+  *reinterpret_cast<u32x4 *>(p) = w;
+}
+template <> __device__ __forceinline__ void storev<float, 4>(float *p, const FV<4> &x) {
+  *reinterpret_cast<float4 *>(p) = make_float4(x.v[0], x.v[1], x.v[2], x.v[3]);
+}
+template <> __device__ __forceinline__ void storev<float, 8>(float *p, const FV<8> &x) {
+  reinterpret_cast<float4 *>(p)[0] = make_float4(x.v[0], x.v[1], x.v[2], x.v[3]);
+  reinterpret_cast<float4 *>(p)[1] = make_float4(x.v[4], x.v[5], x.v[6], x.v[7]);
+}
+
 // Workgroup x of a per-(chunk, query head) grid -> (hq, c); false for the
 // padding workgroups.  Two orders, chosen on the host by grid size:
 //  * chunk order (c fastest): for a grid the GPU holds at once; whole chunks
@@ -98,7 +144,7 @@ __device__ __forceinline__ float wave_inclusive_scan(float x) {
 }
 
 // Phase A: sum of g (per channel) and of g_scalar over each chunk.
-// grid (cg.size(), nseg), 256 threads; a thread owns 4 channels.
+// grid (cg.size(), nseg), 256 threads; a thread owns CPT channels.
 template <typename TE, int KD>
 __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
                                                     const TE *__restrict__ gs,
@@ -114,37 +160,30 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
   const int64_t r0 = bos + (int64_t)c * CHUNK;
   if (r0 >= eos) return;
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
-  constexpr int NQ = KD / 4, NG = 256 / NQ;
-  const int q4 = threadIdx.x % NQ, grp = threadIdx.x / NQ;
+  constexpr int CPT = cpt<TE>(), NQ = KD / CPT, NG = 256 / NQ;
+  const int cgi = threadIdx.x % NQ, grp = threadIdx.x / NQ;
   // compile-time row count with a guard: the thread's loads go out together
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float4 xs[CHUNK / NG];
+  FV<CPT> xs[CHUNK / NG];
 #pragma unroll
   for (int i = 0; i < CHUNK / NG; ++i) {
     const int r = grp + i * NG;
-    xs[i] = r < nrow ? load4<TE>(g + ((r0 + r) * HQ + hq) * KD + 4 * q4) : make_float4(0.f, 0.f, 0.f, 0.f);
+    xs[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
   }
+  FV<CPT> acc = zerov<CPT>();
 #pragma unroll
-  for (int i = 0; i < CHUNK / NG; ++i) {
-    acc.x += xs[i].x;
-    acc.y += xs[i].y;
-    acc.z += xs[i].z;
-    acc.w += xs[i].w;
-  }
-  __shared__ float4 red[NG][NQ];
-  red[grp][q4] = acc;
+  for (int i = 0; i < CHUNK / NG; ++i)
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc.v[j] += xs[i].v[j];
+  __shared__ FV<CPT> red[NG][NQ];
+  red[grp][cgi] = acc;
   __syncthreads();
   const int64_t cidx = (int64_t)s * NCmax + c;
   if (grp == 0) {
 #pragma unroll
-    for (int q = 1; q < NG; ++q) {
-      const float4 y = red[q][q4];
-      acc.x += y.x;
-      acc.y += y.y;
-      acc.z += y.z;
-      acc.w += y.w;
-    }
-    *reinterpret_cast<float4 *>(csum + (cidx * HQ + hq) * KD + 4 * q4) = acc;
+    for (int q = 1; q < NG; ++q)
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) acc.v[j] += red[q][cgi].v[j];
+    storev<float, CPT>(csum + (cidx * HQ + hq) * KD + CPT * cgi, acc);
   }
   if (gs != nullptr && threadIdx.x < 64) {
     float a = (int)threadIdx.x < nrow ? Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.f;
@@ -241,44 +280,33 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
   }
 }
 
-// In-chunk running sums of g for 4 channels of one chunk (shared by the two
+// In-chunk running sums of g for CPT channels of one chunk (shared by the two
 // phase-C kernels): rows are split into NG groups of RPG consecutive rows;
 // each thread scans its group, the group totals go through LDS.  Returns in
 // p2[i] the running sum at row grp*RPG + i in log2 units (offset included).
 template <typename TE, int KD>
 struct ChunkScan {
-  static constexpr int NQ = KD / 4, NG = 256 / NQ, RPG = CHUNK / NG;
+  static constexpr int CPT = cpt<TE>(), NQ = KD / CPT, NG = 256 / NQ, RPG = CHUNK / NG;
   __device__ __forceinline__ static void run(const TE *g, int64_t r0, int nrow, int HQ, int hq,
-                                             int q4, int grp, float4 base, float4 (&p2)[RPG]) {
-    __shared__ float4 tot[NG][NQ];
+                                             int cgi, int grp, FV<CPT> base, FV<CPT> (&p2)[RPG]) {
+    __shared__ FV<CPT> tot[NG][NQ];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
       const int r = grp * RPG + i;
-      p2[i] = r < nrow ? load4<TE>(g + ((r0 + r) * HQ + hq) * KD + 4 * q4)
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      if (i > 0) {
-        p2[i].x += p2[i - 1].x;
-        p2[i].y += p2[i - 1].y;
-        p2[i].z += p2[i - 1].z;
-        p2[i].w += p2[i - 1].w;
-      }
-    }
-    tot[grp][q4] = p2[RPG - 1];
-    __syncthreads();
-    for (int q = 0; q < grp; ++q) {
-      const float4 y = tot[q][q4];
-      base.x += y.x;
-      base.y += y.y;
-      base.z += y.z;
-      base.w += y.w;
-    }
+      p2[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
+      if (i > 0)
 #pragma unroll
-    for (int i = 0; i < RPG; ++i) {
-      p2[i].x = (base.x + p2[i].x) * LOG2E;
-      p2[i].y = (base.y + p2[i].y) * LOG2E;
-      p2[i].z = (base.z + p2[i].z) * LOG2E;
-      p2[i].w = (base.w + p2[i].w) * LOG2E;
+        for (int j = 0; j < CPT; ++j) p2[i].v[j] += p2[i - 1].v[j];
     }
+    tot[grp][cgi] = p2[RPG - 1];
+    __syncthreads();
+    for (int q = 0; q < grp; ++q)
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) base.v[j] += tot[q][cgi].v[j];
+#pragma unroll
+    for (int i = 0; i < RPG; ++i)
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) p2[i].v[j] = (base.v[j] + p2[i].v[j]) * LOG2E;
   }
 };
 
@@ -297,7 +325,7 @@ struct ChunkScan {
 // gsum of the token split into two halves, 0 without a gate), so a key tile
 // is one contiguous block and the attention kernel's score product also
 // subtracts the row shift and the gate.  Float operands keep [ntok, HQ, KD].
-// grid (cg.size(), nseg), 256 threads; a thread owns 4 channels.
+// grid (cg.size(), nseg), 256 threads; a thread owns CPT channels.
 template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
 __global__ __launch_bounds__(256) void k_prefill_operands(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ g,
@@ -317,35 +345,32 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
   const int h = hq / (HQ / H);
   typedef ChunkScan<TE, KD> CS;
-  const int q4 = threadIdx.x % CS::NQ, grp = threadIdx.x / CS::NQ;
+  constexpr int CPT = CS::CPT;
+  const int cgi = threadIdx.x % CS::NQ, grp = threadIdx.x / CS::NQ;
   const int64_t cidx = (int64_t)s * NCmax + c;
-  const int64_t cq = (int64_t)s * NCmax + (c & ~1);
-  const float4 base = *reinterpret_cast<const float4 *>(off + (cidx * HQ + hq) * KD + 4 * q4);
-  const float4 A = *reinterpret_cast<const float4 *>(anch + (cidx * HQ + hq) * KD + 4 * q4);
-  const float4 RQ = *reinterpret_cast<const float4 *>(anch + (cq * HQ + hq) * KD + 4 * q4);
-  float4 p2[CS::RPG];
-  CS::run(g, r0, nrow, HQ, hq, q4, grp, base, p2);
+  const FV<CPT> base = loadv<float, CPT>(off + (cidx * HQ + hq) * KD + CPT * cgi);
+  const FV<CPT> A = loadv<float, CPT>(anch + (cidx * HQ + hq) * KD + CPT * cgi);
+  FV<CPT> p2[CS::RPG];
+  CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
 #pragma unroll
   for (int i = 0; i < CS::RPG; ++i) {
     const int r = grp * CS::RPG + i;
     if (r < nrow) {
       const int64_t t = r0 + r;
       if (!HM) {  // half operands: the attention kernel forms q_hat itself
-        const float4 qv = load4<TE>(q + (t * HQ + hq) * KD + 4 * q4);
-        float4 qo;
-        qo.x = qv.x * fast_exp2(p2[i].x - RQ.x) * qscale;
-        qo.y = qv.y * fast_exp2(p2[i].y - RQ.y) * qscale;
-        qo.z = qv.z * fast_exp2(p2[i].z - RQ.z) * qscale;
-        qo.w = qv.w * fast_exp2(p2[i].w - RQ.w) * qscale;
-        store4<TO>(qh + (t * HQ + hq) * KD + 4 * q4, qo);
+        const int64_t cq = (int64_t)s * NCmax + (c & ~1);
+        const FV<CPT> RQ = loadv<float, CPT>(anch + (cq * HQ + hq) * KD + CPT * cgi);
+        const FV<CPT> qv = loadv<TE, CPT>(q + (t * HQ + hq) * KD + CPT * cgi);
+        FV<CPT> qo;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) qo.v[j] = qv.v[j] * fast_exp2(p2[i].v[j] - RQ.v[j]) * qscale;
+        storev<TO, CPT>(qh + (t * HQ + hq) * KD + CPT * cgi, qo);
       }
-      const float4 kv = load4<TE>(k + (t * H + h) * KD + 4 * q4);
-      float4 ko;
-      ko.x = kv.x * fast_exp2(A.x - p2[i].x);
-      ko.y = kv.y * fast_exp2(A.y - p2[i].y);
-      ko.z = kv.z * fast_exp2(A.z - p2[i].z);
-      ko.w = kv.w * fast_exp2(A.w - p2[i].w);
-      store4<TO>(kt + (HM ? (hq * ntok + t) : (t * HQ + hq)) * KX + 4 * q4, ko);
+      const FV<CPT> kv = loadv<TE, CPT>(k + (t * H + h) * KD + CPT * cgi);
+      FV<CPT> ko;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) ko.v[j] = kv.v[j] * fast_exp2(A.v[j] - p2[i].v[j]);
+      storev<TO, CPT>(kt + (HM ? (hq * ntok + t) : (t * HQ + hq)) * KX + CPT * cgi, ko);
     }
   }
   if (threadIdx.x < 64) {
@@ -383,15 +408,16 @@ __global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
   if (r0 >= eos) return;
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
   typedef ChunkScan<TE, KD> CS;
-  const int q4 = threadIdx.x % CS::NQ, grp = threadIdx.x / CS::NQ;
+  constexpr int CPT = CS::CPT;
+  const int cgi = threadIdx.x % CS::NQ, grp = threadIdx.x / CS::NQ;
   const int64_t cidx = (int64_t)s * NCmax + c;
-  const float4 base = *reinterpret_cast<const float4 *>(off + (cidx * HQ + hq) * KD + 4 * q4);
-  float4 p2[CS::RPG];
-  CS::run(g, r0, nrow, HQ, hq, q4, grp, base, p2);
+  const FV<CPT> base = loadv<float, CPT>(off + (cidx * HQ + hq) * KD + CPT * cgi);
+  FV<CPT> p2[CS::RPG];
+  CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
 #pragma unroll
   for (int i = 0; i < CS::RPG; ++i) {
     const int r = grp * CS::RPG + i;
-    if (r < nrow) *reinterpret_cast<float4 *>(P2 + ((r0 + r) * HQ + hq) * KD + 4 * q4) = p2[i];
+    if (r < nrow) storev<float, CPT>(P2 + ((r0 + r) * HQ + hq) * KD + CPT * cgi, p2[i]);
   }
 }
 
