@@ -23,38 +23,6 @@ namespace wa {
 
 namespace {
 
-template <typename TE>
-__device__ __forceinline__ float4 load4(const TE *p);
-template <>
-__device__ __forceinline__ float4 load4<bf16_t>(const bf16_t *p) {
-  u32x2 w = *reinterpret_cast<const u32x2 *>(p);
-  return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-}
-template <>
-__device__ __forceinline__ float4 load4<float>(const float *p) {
-  return *reinterpret_cast<const float4 *>(p);
-}
-template <typename TE>
-__device__ __forceinline__ void store4(TE *p, float4 x);
-template <>
-__device__ __forceinline__ void store4<bf16_t>(bf16_t *p, float4 x) {
-  u32x2 w;
-  w.x = pack_bf16x2(x.x, x.y);
-  w.y = pack_bf16x2(x.z, x.w);
-  *reinterpret_cast<u32x2 *>(p) = w;
-}
-template <>
-__device__ __forceinline__ void store4<_Float16>(_Float16 *p, float4 x) {
-  u32x2 w;
-  w.x = pack_f16x2(x.x, x.y);
-  w.y = pack_f16x2(x.z, x.w);
-  *reinterpret_cast<u32x2 *>(p) = w;
-}
-template <>
-__device__ __forceinline__ void store4<float>(float *p, float4 x) {
-  *reinterpret_cast<float4 *>(p) = x;
-}
-
 // N consecutive channels as floats; the pre-pass moves 16 bytes of its input
 // type per access (CPT = 8 bfloat16 or 4 float channels per thread).
 template <typename TE> constexpr int cpt() { return 16 / (int)sizeof(TE); }
@@ -423,7 +391,7 @@ __global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
 
 // Decode cache: r_cache[c] = P2 at the chunk's last token (copied), and
 // k_tilde = k * 2^(r_cache[c] - P2) in the operand type.
-// grid (cg.size(), B), 256 threads; each thread owns 4 channels.
+// grid (cg.size(), B), 256 threads; each thread owns CPT channels.
 template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
 __global__ __launch_bounds__(256) void k_build_cache(const TE *__restrict__ k,
                                                      const float *__restrict__ P2,
@@ -435,24 +403,29 @@ __global__ __launch_bounds__(256) void k_build_cache(const TE *__restrict__ k,
   const int64_t r0 = (int64_t)c * CHUNK;
   const int nrow = (T - r0) < CHUNK ? (int)(T - r0) : CHUNK;
   const int h = hq / (HQ / H);
-  constexpr int NQ = KD / 4;
-  constexpr int NRG = 256 / NQ;
-  const int n4 = (threadIdx.x % NQ) * 4, rg = threadIdx.x / NQ;
+  constexpr int CPT = cpt<TE>(), NQ = KD / CPT, NRG = 256 / NQ, RPT = CHUNK / NRG;
+  const int n0 = (threadIdx.x % NQ) * CPT, rg = threadIdx.x / NQ;
   const int64_t tb = (int64_t)b * T;
-  const float4 R =
-      *reinterpret_cast<const float4 *>(P2 + ((tb + r0 + nrow - 1) * HQ + hq) * KD + n4);
-  if (rg == 0)
-    *reinterpret_cast<float4 *>(rc + (((int64_t)b * NC + c) * HQ + hq) * KD + n4) = R;
-  for (int r = rg; r < nrow; r += NRG) {
+  const FV<CPT> R = loadv<float, CPT>(P2 + ((tb + r0 + nrow - 1) * HQ + hq) * KD + n0);
+  if (rg == 0) storev<float, CPT>(rc + (((int64_t)b * NC + c) * HQ + hq) * KD + n0, R);
+  // compile-time row count with a guard: the thread's loads go out together
+  FV<CPT> p[RPT], kv[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + i * NRG;
     const int64_t t = tb + r0 + r;
-    const float4 p = *reinterpret_cast<const float4 *>(P2 + (t * HQ + hq) * KD + n4);
-    const float4 kv = load4<TE>(k + (t * H + h) * KD + n4);
-    float4 out;
-    out.x = kv.x * fast_exp2(R.x - p.x);
-    out.y = kv.y * fast_exp2(R.y - p.y);
-    out.z = kv.z * fast_exp2(R.z - p.z);
-    out.w = kv.w * fast_exp2(R.w - p.w);
-    store4<TO>(kt + (t * HQ + hq) * KD + n4, out);
+    p[i] = r < nrow ? loadv<float, CPT>(P2 + (t * HQ + hq) * KD + n0) : zerov<CPT>();
+    kv[i] = r < nrow ? loadv<TE, CPT>(k + (t * H + h) * KD + n0) : zerov<CPT>();
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int r = rg + i * NRG;
+    if (r < nrow) {
+      FV<CPT> out;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j) out.v[j] = kv[i].v[j] * fast_exp2(R.v[j] - p[i].v[j]);
+      storev<TO, CPT>(kt + ((tb + r0 + r) * HQ + hq) * KD + n0, out);
+    }
   }
 }
 
