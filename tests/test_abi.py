@@ -75,6 +75,12 @@ def test_fwd_rejects_bad_shapes(lib):
     assert b"too long" in lib.wall_attn_last_error()
     assert lib.wall_attn_fwd_workspace_bytes(1, (1 << 19) - 64, 16, 4, 128, 128, 0, 0, 0) > 0
     assert lib.wall_attn_fwd_workspace_bytes(1, 1 << 19, 16, 4, 128, 128, 0, 0, 1) > 0  # fp32: 64-bit
+    # launch-grid limits: at most 65535 segments, HQ*(ceil(max_seqlen/64)+8)*segments < 2^31
+    assert fwd(lib, B=1, T=70000, cu=FAKE, nseq=70000, maxlen=1, dtype=1) == 2
+    assert b"launch grid" in lib.wall_attn_last_error()
+    assert fwd(lib, B=65535, T=4096, HQ=1024, H=1024, dtype=1) == 2
+    assert b"launch grid" in lib.wall_attn_last_error()
+    assert lib.wall_attn_fwd_workspace_bytes(65535, 4096, 1024, 1024, 64, 64, 0, 0, 1) == 0
 
 
 def test_fwd_rejects_bad_pointers_and_workspace(lib):
@@ -108,6 +114,8 @@ def test_cache_and_decode_reject_bad_arguments(lib):
     assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 3, 64, 64, 0, None) == 1   # HQ % H
     assert bk(None, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 64, 0, None) == 1
     assert bk(FAKE, FAKE, FAKE + 4, FAKE, 1, 128, 4, 2, 64, 64, 0, None) == 1
+    assert bk(FAKE, FAKE, FAKE, FAKE, 70000, 128, 4, 2, 64, 64, 1, None) == 2      # B > 65535
+    assert bk(FAKE, FAKE, FAKE, FAKE, 2, 1 << 26, 1024, 8, 64, 64, 1, None) == 2   # grid x
     dec = lib.wall_attn_decode
 
     def d(**kw):
@@ -124,6 +132,7 @@ def test_cache_and_decode_reject_bad_arguments(lib):
     assert d(o=FAKE + 2) == 1
     assert d(wsb=16) == 4
     assert d(dt=3) == 2
+    assert d(T=1 << 20, HQ=32, H=8) == 2      # one batch row of the half cache beyond 2^31 bytes
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors():
