@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     constexpr bool RB = decltype(rb_c)::value;
     constexpr int NP = 2 * NMB;
     constexpr FusedOrder<NKS, NP, 4> FO{};
-    constexpr int KAHEAD = 4, VAHEAD = 4, RAHEAD = 2, DSLOT = 4;
+    constexpr int KAHEAD = 4, VAHEAD = 4, RAHEAD = 1, DSLOT = 4;
     constexpr int E = 16;                 // exponentials of the tile
     static_assert(DSLOT + NDM <= FO.N, "every load needs a slot");
     f16x8 ka[NKS];
