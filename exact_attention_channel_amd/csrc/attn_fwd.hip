@@ -3,15 +3,18 @@
 // Wall Attention README, introduction: the score of query i and key j weights
 // channel n of q_i . k_j by exp(P[i,n] - P[j,n]), P the running sum of the
 // learned decay g; "Usage" adds GQA, the scalar gate g_scalar, sink_bias,
-// window_size and cu_seqlens.  The pre-pass (prefix.hip) has already written
+// window_size and cu_seqlens.  With the operands
 //   q_hat_i   = q_i * 2^(P2_i - RQ_I) * scale * log2(e)     (query tile anchor RQ_I)
 //   k_tilde_j = k_j * 2^(R_J - P2_j)                        (key chunk anchor R_J)
-// so for a query tile I and a 64-key chunk J the decayed scores are one dense
-// product: S = (q_hat * d_IJ) . k_tilde^T with d_IJ[n] = 2^(RQ_I[n] - R_J[n]),
-// K exponentials per tile pair instead of K per (i, j) pair.  Scores are in
-// log2 units, so the online softmax (FlashAttention's running max and sum,
-// see the FlashAttention papers' tiling with rescaled partial outputs) uses
-// exp2 directly.
+// (k_tilde written by the pre-pass, prefix.hip; q_hat formed per query tile
+// here from q, g and the pre-pass's chunk offsets, or written by the
+// pre-pass for fp32 inputs) the decayed scores of a query tile I and a
+// 64-key chunk J are one dense product: S = (q_hat * d_IJ) . k_tilde^T with
+// d_IJ[n] = 2^(RQ_I[n] - R_J[n]), K exponentials per tile pair instead of K
+// per (i, j) pair.  Scores are in log2 units, so the softmax uses exp2
+// directly: the fp32 kernel keeps FlashAttention's running max and sum (the
+// FlashAttention papers' tiling with rescaled partial outputs), the bf16
+// kernel a fixed per-row reference max (see its sweep below).
 //
 // bf16 inputs: the rescaled q/k operands are IEEE half (3 more mantissa bits
 // than bfloat16, which keeps the rounding of large decayed scores within
