@@ -41,3 +41,40 @@ def test_default_workloads_stay_below_rebalancing():
     timing is the common path's."""
     x = W.make_prefill(W.PREFILL_T8192_BF16)
     assert _anchor_gaps(x) <= 8
+
+
+def _pairs(lengths, window=0):
+    """Allowed (i, j) pairs per head: 0 <= i - j < window (no window: i - j >= 0)."""
+    tot = 0
+    for n in lengths:
+        if window <= 0 or n <= window:
+            tot += n * (n + 1) // 2
+        else:
+            tot += window * (window + 1) // 2 + (n - window) * window
+    return tot
+
+
+def test_workload_recipes_match_the_stated_configurations():
+    """Shapes, seeded varlen lengths and algorithmic work of the five workloads
+    (the counting rule: 2*HQ*(K+V) FLOPs per allowed pair)."""
+    c = W.PREFILL_T8192_BF16
+    assert (c.B, c.T, c.HQ, c.H, c.K, c.V, c.window) == (1, 8192, 16, 4, 128, 128, 0)
+    assert 2 * c.HQ * (c.K + c.V) * _pairs([c.T]) == 274_911_461_376
+    v = W.VARLEN_W2048_BF16
+    lens = W.varlen_lengths(v)
+    assert lens == [3312, 4076, 1218, 2710, 896, 2878, 3871, 3993, 3569, 1298, 2295, 2293, 1177,
+                    3015, 822, 1209]
+    assert sum(lens) == 38_632 and all(512 <= n <= 4096 for n in lens)
+    assert _pairs(lens, v.window) == 48_349_525
+    assert round(2 * v.HQ * (v.K + v.V) * _pairs(lens, v.window) / 1e9, 2) == 792.16
+    u = W.PREFILL_T1024_BF16
+    assert (u.B, u.T, u.HQ, u.H, u.K, u.V) == (2, 1024, 8, 4, 64, 64)
+    assert 2 * u.HQ * (u.K + u.V) * u.B * _pairs([u.T]) == 2_149_580_800
+    t = W.PREFILL_T128_FP32
+    assert (t.B, t.T, t.HQ, t.H, t.K, t.V, t.dtype) == (1, 128, 2, 1, 64, 64, torch.float32)
+    d = W.DECODE_T32768_BF16
+    assert (d.B, d.T_kv, d.HQ, d.H, d.K, d.V, d.C) == (64, 32768, 32, 8, 128, 128, 64)
+    cache_bytes = (d.B * d.T_kv * d.HQ * d.K * 2 + d.B * d.T_kv * d.H * d.V * 2
+                   + d.B * (d.T_kv // d.C) * d.HQ * d.K * 4)
+    step_bytes = cache_bytes + d.B * d.HQ * d.K * 2 + d.B * d.HQ * d.K * 4 + d.B * d.HQ * d.V * 2
+    assert step_bytes == 22_013_804_544
