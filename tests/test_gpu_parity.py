@@ -107,6 +107,13 @@ SMALL = [
     # (key/value head, chunk) pair order
     cfg("bf16_varlen64_gqa4_pair_order", 1, 0, 8, 2, 64, 64, torch.bfloat16, nseq=64, len_lo=1,
         len_hi=700, g_scalar_std=0.01, sink=True, seed=26),
+    # long enough for steady tile pairs with K=128, V=64 and with K=64, V=128
+    # (the latter windowed: ceil((W-1)/32) odd, so the window start is rounded
+    # down to a chunk)
+    cfg("bf16_T700_K128_V64_gqa2_gate_sink", 1, 700, 4, 2, 128, 64, torch.bfloat16,
+        g_mode="neg_softplus", g_std=0.05, g_scalar_std=0.01, sink=True, seed=27),
+    cfg("bf16_varlen_K64_V128_window200", 1, 0, 4, 1, 64, 128, torch.bfloat16, nseq=6,
+        len_lo=100, len_hi=900, window=200, seed=28),
 ]
 
 
