@@ -19,7 +19,9 @@ Also reported on the same JSON line:
                 sink) per call over its event-timed duration, against HBM
                 peak; the cache build is reported beside it;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores over a row
-                sample of the prefill workload, scaled to TFLOP/s.
+                sample of the prefill workload, scaled to TFLOP/s; the two
+                small workloads (tiny fp32, usage shape) are also timed in
+                full on one host thread (all_configs[].cpu_oracle_1thread).
 The roofline "traffic" fields are HBM bytes per launch measured with rocprof
 counters (profiles/hbm_traffic.json); they are null when the kernel sources
 no longer match the ones the counters were taken on.
@@ -358,6 +360,27 @@ def main():
                       f"{sample_flops / 1e9:.1f} GFLOP algorithmic) in {dt:.2f} s; "
                       "TFLOP/s = sample FLOPs / wall time",
         }
+        # the two small workloads in full on one host thread as well
+        n_all = oracle.num_threads()
+        oracle.set_num_threads(1)
+        try:
+            for e in out["all_configs"]:
+                cfg = next((p for p in (W.PREFILL_T128_FP32, W.PREFILL_T1024_BF16)
+                            if p.name == e["workload"]), None)
+                if cfg is None:
+                    continue
+                x1 = W.make_prefill(cfg)
+                t0 = time.perf_counter()
+                oracle.wall_attn(x1["q"], x1["k"], x1["v"], x1["g"], scale=x1["scale"],
+                                 g_scalar=x1["g_scalar"], sink_bias=x1["sink_bias"],
+                                 window_size=x1["window_size"], cu_seqlens=x1["cu_seqlens"])
+                dt1 = time.perf_counter() - t0
+                e["cpu_oracle_1thread"] = {"s": round(dt1, 4),
+                                           "TFLOP/s": round(e["gflop"] * 1e9 / dt1 / 1e12, 6),
+                                           "gpu_speedup": round(dt1 * 1e3 / e["ms"], 1)}
+                log(f"[bench] oracle on one thread, {cfg.name}: {dt1:.3f} s")
+        finally:
+            oracle.set_num_threads(n_all)
     print(json.dumps(out), flush=True)
 
 

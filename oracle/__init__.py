@@ -55,12 +55,19 @@ def _load():
         lib.oracle_decode_cache.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> int:
+    """Threads of the oracle's OpenMP loops from now on; returns the count in force."""
+    return int(_load().oracle_set_num_threads(int(n)))
 
 
 def _f32(x):

@@ -48,6 +48,18 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads the loops below use from now on (n > 0); returns the count in force.
+   Only the timing of the oracle changes, not what it computes. */
+int oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+  return omp_get_max_threads();
+#else
+  (void)n;
+  return 1;
+#endif
+}
+
 /* Segment s of the packed token axis: [bos, eos). */
 static void segment(int64_t s, int64_t T, const int32_t *cu, int64_t *bos, int64_t *eos) {
   if (cu) {
