@@ -171,7 +171,12 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index
   const int col = lane & 31, half = lane >> 5;
-  const int hq = blockIdx.x % HQ;
+  // Workgroups go to the 8 XCDs round robin; with HQ a multiple of 8, XCD x
+  // serves query heads x*HQ/8 .. (x+1)*HQ/8 - 1, neighbours that share
+  // key/value heads, so the value tiles they read meet in one L2 (packed
+  // varlen workload: 2-4% faster; neutral at HQ = 16).
+  const int hq = HQ % 8 == 0 ? (int)(blockIdx.x % 8) * (HQ / 8) + (int)((blockIdx.x % HQ) / 8)
+                             : (int)(blockIdx.x % HQ);
   const int rest = blockIdx.x / HQ;
   // Without a window, longest query tiles first over all segments (balance:
   // a tile's key count grows with I).  With a window every tile sees about
