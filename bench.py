@@ -7,7 +7,11 @@ T = 8K and single-step decode GB/s over a 32K-token cache.
 One "step" is one call of wall_attn_fwd (running-sum pre-pass + attention)
 on the long-context workload B=1, T=8192, HQ=16, H=4, K=V=128, bf16, with
 g = -0.05*softplus(N(0,1)), g_scalar and sink_bias (inputs resident in HBM
-before timing starts).  ``value`` is its throughput in algorithmic TFLOP/s:
+before timing starts).  After the warm-up steps, untimed steps run for
+--settle seconds (the clocks ramp up over the first tens of milliseconds);
+the timed steps are then interleaved in blocks with blocks of the
+pre-pass alone and of the attention kernel alone, so the three figures see
+the same clocks.  ``value`` is its throughput in algorithmic TFLOP/s:
 2*HQ*(K+V) per visible (query, key) pair, only causal pairs counted.
 
 Also reported on the same JSON line:
@@ -15,8 +19,10 @@ Also reported on the same JSON line:
                 HIP events on the launch stream, against the MI355X dense
                 fp16/bf16 MFMA peak;
   decode        wall_attn_decode on B=64, T_kv=32768, HQ=32, H=8, K=V=128,
-                C=64: algorithmic bytes (k_tilde, v, r_cache, q, p_curr, o,
-                sink) per call over its event-timed duration, against HBM
+                C=64, for each cache element type (float32 -- the format
+                that reproduces the forward on this workload -- float16,
+                bfloat16): algorithmic bytes (k_tilde, v, r_cache, q, p_curr,
+                o, sink) per call over its event-timed duration, against HBM
                 peak; the cache build is reported beside it;
   cpu_baseline  the fp64 CPU oracle timed on this host's cores over a row
                 sample of the prefill workload, scaled to TFLOP/s; the two
@@ -48,6 +54,8 @@ def parse():
     # with 5 warm-up steps (~2 ms) the first timed steps of the 8K prefill ran
     # ~15% slower than later ones
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle", type=float, default=0.5,
+                    help="seconds of untimed launches after the warm-up steps, before timing")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=1,
@@ -64,7 +72,9 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "hbm_traffic.json")
 # sources whose kernels the recorded counters describe
 TRAFFIC_SOURCES = {
     "attend": ["attn_fwd.hip", "common.h", "launch.h"],
-    "decode_split": ["decode.hip", "common.h", "launch.h"],
+    "decode_split_float32": ["decode_kernels.h", "decode.hip", "common.h", "launch.h"],
+    "decode_split_float16": ["decode_kernels.h", "decode.hip", "common.h", "launch.h"],
+    "decode_split_bfloat16": ["decode_kernels.h", "decode.hip", "common.h", "launch.h"],
 }
 
 
@@ -157,6 +167,32 @@ def time_prefill(cfg, lib, wa, W, torch, dev, stream, steps, warmup):
     return ms, 2.0 * HQ * (K + V) * causal_pairs(lengths, window)
 
 
+def settle_clocks(fn, seconds, torch):
+    """Untimed launches of fn until `seconds` of wall time have passed (the
+    GPU clocks ramp up over the first tens of milliseconds of work); returns
+    the time spent."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def interleaved_ms(fns, steps, torch, blocks=5):
+    """Average ms per launch of each fn: `steps` launches of each, in `blocks`
+    rounds that cycle through the fns, every round's launches of one fn timed
+    between two events on the current stream."""
+    n = [steps // blocks + (1 if b < steps % blocks else 0) for b in range(blocks)]
+    tot = [0.0] * len(fns)
+    for nb in n:
+        if nb == 0:
+            continue
+        for i, fn in enumerate(fns):
+            tot[i] += event_time_ms(fn, nb, torch) * nb
+    return [t / steps for t in tot]
+
+
 def log(msg):
     sys.stderr.write(msg + "\n")
     sys.stderr.flush()
@@ -223,13 +259,13 @@ def main():
     flops = 2.0 * HQ * (K + V) * causal_pairs([T] * B)
     for _ in range(args.warmup):
         fwd()
-    torch.cuda.synchronize()
-    # timed region: exactly `steps` full forward passes between events
-    ms_step = event_time_ms(fwd, args.steps, torch)
-    log(f"[bench] prefill step {ms_step:.4f} ms")
-    ms_prep = event_time_ms(prepare, args.steps, torch)
-    ms_attn = event_time_ms(attend, args.steps, torch)
-    log(f"[bench] prepare {ms_prep:.4f} ms, attend {ms_attn:.4f} ms")
+    settle_s = settle_clocks(fwd, args.settle, torch)
+    # timed region: exactly `steps` full forward passes, in blocks interleaved
+    # with blocks of the two stages alone, so that all three see the same
+    # clocks; each block is bracketed by synchronisations and events
+    ms_step, ms_prep, ms_attn = interleaved_ms([fwd, prepare, attend], args.steps, torch)
+    log(f"[bench] prefill step {ms_step:.4f} ms; prepare {ms_prep:.4f} ms, attend {ms_attn:.4f} ms "
+        f"(after {args.warmup} warm-up steps and {settle_s:.2f} s of clock settling)")
     tflops = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (ms_attn * 1e-3) / 1e12
     del ws, o, lse, x
@@ -242,6 +278,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": round(settle_s, 3),
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -282,63 +319,72 @@ def main():
     # ------------------------------------------------------------------ decode
     if not args.no_decode:
         d = W.DECODE_T32768_BF16
-        log(f"[bench] decode workload {d.name}: generating inputs on the GPU")
+        log(f"[bench] decode workload {d.name}: drawing inputs (one host thread per batch row)")
         y = W.make_decode(d, device=dev)
         P = wa.wall_attn_prefix_log2(y["g"])
         del y["g"]
         torch.cuda.empty_cache()
-        kt, rc_ = wa.build_wall_kv_cache(y["k"], P, chunk_size=d.C)
         pc = P[:, -1:].contiguous()
-        def build():
-            r = lib.wall_attn_build_kv_cache(ptr(y["k"]), ptr(P), ptr(kt), ptr(rc_), d.B, d.T_kv,
-                                             d.HQ, d.H, d.K, d.C, wa.WA_BF16, stream)
-            if r:
-                raise RuntimeError(lib.wall_attn_last_error().decode())
-
-        build_ms = event_time_ms(build, 3, torch)
-        del P
-        torch.cuda.empty_cache()
         do = torch.empty(d.B, 1, d.HQ, d.V, dtype=d.dtype, device=dev)
         dl = torch.empty(d.B, 1, d.HQ, dtype=torch.float32, device=dev)
         dwb = lib.wall_attn_decode_workspace_bytes(d.B, d.T_kv, d.HQ, d.H, d.K, d.V, d.C)
         dws = torch.empty(dwb, dtype=torch.uint8, device=dev)
         dscale = float(y["scale"])
+        out["decode"] = {}
+        # float32 cache first: the format that reproduces the forward on this
+        # workload (the headline decode figure); the 16-bit caches for context
+        for cname, ct, code in (("float32", torch.float32, wa.WA_F32),
+                                ("float16", torch.float16, wa.WA_F16),
+                                ("bfloat16", torch.bfloat16, wa.WA_BF16)):
+            kt, rc_ = wa.build_wall_kv_cache(y["k"], P, chunk_size=d.C, cache_dtype=ct)
 
-        def dec():
-            r = lib.wall_attn_decode(ptr(y["q"]), ptr(y["v"]), ptr(pc), ptr(kt), ptr(rc_),
-                                     ptr(y["sink_bias"]), ptr(do), ptr(dl), d.B, d.T_kv, d.HQ,
-                                     d.H, d.K, d.V, d.C, dscale, wa.WA_BF16, ptr(dws), dwb,
-                                     stream)
-            if r:
-                raise RuntimeError(lib.wall_attn_last_error().decode())
+            def build():
+                r = lib.wall_attn_build_kv_cache(ptr(y["k"]), ptr(P), ptr(kt), ptr(rc_), d.B,
+                                                 d.T_kv, d.HQ, d.H, d.K, d.C, wa.WA_BF16, code,
+                                                 stream)
+                if r:
+                    raise RuntimeError(lib.wall_attn_last_error().decode())
 
-        for _ in range(args.warmup):
-            dec()
-        dms = event_time_ms(dec, args.steps, torch)
-        nc = -(-d.T_kv // d.C)
-        dbytes = (kt.numel() * kt.element_size() + y["v"].numel() * 2 + rc_.numel() * 4
-                  + y["q"].numel() * 2 + pc.numel() * 4 + do.numel() * 2
-                  + (0 if y["sink_bias"] is None else d.HQ * 4))
-        assert rc_.shape[1] == nc
-        gbs = dbytes / (dms * 1e-3) / 1e9
-        log(f"[bench] decode {dms:.4f} ms, {gbs:.1f} GB/s; cache build {build_ms:.3f} ms")
-        k_bytes = y["k"].numel() * 2
-        build_bytes = (k_bytes + d.B * d.T_kv * d.HQ * d.K * 4 + kt.numel() * kt.element_size()
-                       + rc_.numel() * 4)
-        out["decode"] = {
-            "workload": d.name, "metric": "decode GB/s", "value": round(gbs, 1), "unit": "GB/s",
-            "ms_per_call": round(dms, 4), "bytes_per_call": dbytes,
-            "roofline": {"kernel": "k_decode_split + k_decode_combine (wall_attn_decode)",
-                         "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "traffic": recorded_traffic("decode_split")},
-            "cache_build": {"ms": round(build_ms, 3),
-                            "GB/s": round(build_bytes / (build_ms * 1e-3) / 1e9, 1)},
-        }
-        out["all_configs"].append({"workload": d.name, "call": "wall_attn_decode", "dtype": "bf16",
-                                   "ms": round(dms, 4), "GB/s": round(gbs, 1),
-                                   "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
-        del kt, rc_, y, dws, do, dl, pc
+            def dec():
+                r = lib.wall_attn_decode(ptr(y["q"]), ptr(y["v"]), ptr(pc), ptr(kt), ptr(rc_),
+                                         ptr(y["sink_bias"]), ptr(do), ptr(dl), d.B, d.T_kv, d.HQ,
+                                         d.H, d.K, d.V, d.C, dscale, wa.WA_BF16, code, ptr(dws),
+                                         dwb, stream)
+                if r:
+                    raise RuntimeError(lib.wall_attn_last_error().decode())
+
+            build_ms = event_time_ms(build, 3, torch)
+            for _ in range(args.warmup):
+                dec()
+            dms = event_time_ms(dec, args.steps, torch)
+            nc = -(-d.T_kv // d.C)
+            assert rc_.shape[1] == nc
+            dbytes = (kt.numel() * kt.element_size() + y["v"].numel() * 2 + rc_.numel() * 4
+                      + y["q"].numel() * 2 + pc.numel() * 4 + do.numel() * 2
+                      + (0 if y["sink_bias"] is None else d.HQ * 4))
+            gbs = dbytes / (dms * 1e-3) / 1e9
+            build_bytes = (y["k"].numel() * 2 + d.B * d.T_kv * d.HQ * d.K * 4
+                           + kt.numel() * kt.element_size() + rc_.numel() * 4)
+            log(f"[bench] decode ({cname} cache) {dms:.4f} ms, {gbs:.1f} GB/s; "
+                f"cache build {build_ms:.3f} ms")
+            out["decode"][cname + "_cache"] = {
+                "workload": d.name, "cache_dtype": cname, "metric": "decode GB/s",
+                "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(dms, 4),
+                "bytes_per_call": dbytes,
+                "roofline": {"kernel": "k_decode_split + k_decode_combine (wall_attn_decode)",
+                             "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                             "traffic": recorded_traffic("decode_split_" + cname)},
+                "cache_build": {"ms": round(build_ms, 3),
+                                "GB/s": round(build_bytes / (build_ms * 1e-3) / 1e9, 1)},
+            }
+            out["all_configs"].append({"workload": d.name, "call": "wall_attn_decode",
+                                       "dtype": "bf16", "cache_dtype": cname, "ms": round(dms, 4),
+                                       "GB/s": round(gbs, 1),
+                                       "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)})
+            del kt, rc_
+            torch.cuda.empty_cache()
+        del y, dws, do, dl, pc, P
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU baseline

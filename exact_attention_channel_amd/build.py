@@ -13,7 +13,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "prefix.hip", "attn_fwd.hip", "decode.hip"]
+SOURCES = ["api.hip", "prefix.hip", "attn_fwd.hip", "decode.hip", "decode_cache_bf16.hip",
+           "decode_cache_f16.hip", "decode_cache_f32.hip"]
 LIB = os.path.join(HERE, "libwallattn.so")
 ARCH = "gfx950"
 
@@ -32,22 +33,47 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile every source to an object in parallel (one hipcc per file),
+    then link the shared library."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    tag = "%d" % os.getpid()
+    objs, procs = [], []
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    for src in SOURCES:
+        obj = os.path.join(objdir, src.replace(".hip", ".%s.o" % tag))
+        objs.append(obj)
+        procs.append(_run([hipcc(), *flags, *extra, "-c", os.path.join(CSRC, src), "-o", obj], verbose))
+    failed = False
+    noise = "'-packed-fp32-ops' is not a recognized feature"
+    for src, pr in zip(SOURCES, procs):
+        out, _ = pr.communicate()
+        msgs = [l for l in out.splitlines() if noise not in l]
+        if pr.returncode != 0:
+            failed = True
+            sys.stderr.write(f"--- {src}\n" + "\n".join(msgs) + "\n")
+        elif verbose and msgs:
+            print("\n".join(msgs))
+    if failed:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+        raise RuntimeError("hipcc failed building libwallattn.so")
+    tmp = LIB + ".tmp" + tag
+    res = subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp],
+                         capture_output=True, text=True)
+    for o in objs:
+        os.remove(o)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libwallattn.so")
-    if verbose:
-        # the host pass does not know the packed-fp32 feature; that warning is harmless
-        noise = "'-packed-fp32-ops' is not a recognized feature"
-        msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l]
-        if msgs:
-            print("\n".join(msgs))
+        raise RuntimeError("linking libwallattn.so failed")
     os.replace(tmp, LIB)
     return LIB
 

@@ -187,7 +187,10 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   const int I = NQT - 1 - (window > 0 ? rest % NQT : rest / nseg);
   int64_t bos64, eos64;
   segment_bounds(seg, T, cu, bos64, eos64);
-  const int L = (int)(eos64 - bos64);  // sequence length; positions below are relative to bos
+  // sequence length (positions below are relative to bos), clamped to the
+  // NCmax chunks per segment that the workspace holds: with an understated
+  // max_seqlen the rows past it are left unwritten, never read out of bounds
+  const int L = (int)min(eos64 - bos64, (int64_t)NCmax * CHUNK);
   const int nqt = (L + QTILE - 1) / QTILE;
   if (I >= nqt) return;
   const int h = hq / (HQ / H);

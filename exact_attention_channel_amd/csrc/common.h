@@ -104,6 +104,20 @@ __device__ __forceinline__ void segment_bounds(int s, int64_t T, const int32_t *
   eos = uniform64(eos);
 }
 
+// Pool row of token `tok` of batch row b in a decode cache: contiguous
+// [B, T] rows, or pages of page_size rows (a multiple of CHUNK) found through
+// block_table [B, max_blocks] (entries clamped into [0, num_pages) so that no
+// address leaves the pool).
+__device__ __forceinline__ int64_t cache_row(const int32_t *block_table, int64_t max_blocks,
+                                             int page_size, int num_pages, int64_t T, int b,
+                                             int tok) {
+  if (block_table == nullptr) return (int64_t)b * T + tok;
+  const int lp = tok / page_size;
+  int pg = block_table[(int64_t)b * max_blocks + lp];
+  pg = min(max(pg, 0), num_pages - 1);
+  return (int64_t)pg * page_size + (tok - lp * page_size);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

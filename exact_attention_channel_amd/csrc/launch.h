@@ -37,30 +37,64 @@ struct FwdWorkspace {
 };
 
 size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base);
-size_t prefix_workspace_layout(int64_t nseg, int64_t maxlen, int64_t HQ, int64_t K, float **csum,
-                               char *base);
+size_t prefix_workspace_layout(int64_t nseg, int64_t maxlen, int64_t HQ, int64_t K);
 
 hipError_t launch_prefix_phases(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st);
-hipError_t launch_prefix_log2(const void *g, float *P2, const int32_t *cu, int64_t T, int64_t HQ,
-                              int64_t K, int64_t nseg, int64_t maxlen, int dtype, float *csum,
-                              hipStream_t st);
+hipError_t launch_prefix_log2(const void *g, const void *gs, float *P2, float *G2,
+                              const int32_t *cu, int64_t T, int64_t HQ, int64_t K, int64_t nseg,
+                              int64_t maxlen, int dtype, void *ws, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st);
 hipError_t launch_build_cache(const void *k, const float *P2, void *kt, float *rc, int64_t B,
                               int64_t T, int64_t HQ, int64_t H, int64_t K, int dtype,
-                              hipStream_t st);
+                              int cache_dtype, hipStream_t st);
+
+// Element types (the values of the public WA_BF16 / WA_F32 / WA_F16).
+enum { WA_DT_BF16 = 0, WA_DT_F32 = 1, WA_DT_F16 = 2 };
 
 struct DecodeProblem {
   const void *q, *v, *kt;
   const float *p_curr, *rc, *sink;
+  const float *gs_cache, *gs_curr;  // gate running sums (log2 units), or NULL
+  const int32_t *seqlens;           // [B] cached tokens per row, or NULL (all T)
+  const int32_t *block_table;       // [B, max_blocks] pages, or NULL (contiguous rows)
   void *o;
   float *lse;
-  int64_t B, T, HQ, H, K, V;
+  int64_t B, T, HQ, H, K, V;        // T: rows per batch row (contiguous) or max_blocks*page_size
+  int64_t max_blocks, page_size, num_pages;
+  int64_t window;                   // <= 0: none
+  int64_t max_chunks;               // most chunks one row can visit (split planning)
   float scale;
-  int dtype;
+  int dtype, cache_dtype;
 };
-void decode_split_plan(int64_t B, int64_t T, int64_t HQ, int64_t H, int *nsplit,
+
+// Kernel-side view of a decode call (passed by value).
+struct DecodeParams {
+  const void *q, *v, *kt;
+  const float *p_curr, *rc, *gs_cache, *gs_curr;
+  const int32_t *seqlens, *block_table;
+  float *part_o, *part_ml;
+  int64_t T, max_blocks;
+  int page_size, num_pages, NC, HQ, H, nsplit, window;
+  float qscale;
+};
+
+void decode_split_plan(int64_t B, int64_t nchunks, int64_t HQ, int64_t H, int *nsplit,
                        int *chunks_per_split);
-size_t decode_workspace_size(int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t V);
+size_t decode_workspace_size(int64_t B, int64_t nchunks, int64_t HQ, int64_t H, int64_t V);
 hipError_t launch_decode(const DecodeProblem &p, void *ws, hipStream_t st);
+
+// Streaming append of one token per batch row (decode cache).
+struct AppendProblem {
+  const void *k, *v;                // [B,1,H,K], [B,1,H,V] (dtype)
+  const float *p_new;               // [B,1,HQ,K] P2 at the new token
+  const float *gs_new;              // [B,1,HQ] gate running sum at the new token, or NULL
+  void *kt, *vc;                    // cache k_tilde (cache_dtype), v cache (dtype)
+  float *rc, *gs_cache;
+  int32_t *seqlens;
+  const int32_t *block_table;
+  int64_t B, T, HQ, H, K, V, max_blocks, page_size, num_pages;
+  int dtype, cache_dtype;
+};
+hipError_t launch_cache_append(const AppendProblem &p, hipStream_t st);
 
 }  // namespace wa

@@ -54,19 +54,26 @@ template <> __device__ __forceinline__ FV<8> loadv<float, 8>(const float *p) {
   const float4 x = reinterpret_cast<const float4 *>(p)[0], y = reinterpret_cast<const float4 *>(p)[1];
   return FV<8>{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
 }
-template <typename TO, int N> __device__ __forceinline__ void storev(TO *p, const FV<N> &x);
-template <> __device__ __forceinline__ void storev<_Float16, 8>(_Float16 *p, const FV<8> &x) {
-  u32x4 w;
+// N consecutive floats stored as N elements of TO (round to nearest even):
+// 16-bit types pack two per word, N = 8 is one 16-byte store, N = 4 one
+// 8-byte store.
+template <typename TO> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<_Float16>(float lo, float hi) { return pack_f16x2(lo, hi); }
+template <> __device__ __forceinline__ uint32_t pack2<bf16_t>(float lo, float hi) { return pack_bf16x2(lo, hi); }
+template <typename TO, int N> __device__ __forceinline__ void storev(TO *p, const FV<N> &x) {
+  if constexpr (std::is_same<TO, float>::value) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) w[j] = pack_f16x2(x.v[2 * j], x.v[2 * j + 1]);
-  *reinterpret_cast<u32x4 *>(p) = w;
-}
-template <> __device__ __forceinline__ void storev<float, 4>(float *p, const FV<4> &x) {
-  *reinterpret_cast<float4 *>(p) = make_float4(x.v[0], x.v[1], x.v[2], x.v[3]);
-}
-template <> __device__ __forceinline__ void storev<float, 8>(float *p, const FV<8> &x) {
-  reinterpret_cast<float4 *>(p)[0] = make_float4(x.v[0], x.v[1], x.v[2], x.v[3]);
-  reinterpret_cast<float4 *>(p)[1] = make_float4(x.v[4], x.v[5], x.v[6], x.v[7]);
+    for (int j = 0; j < N / 4; ++j)
+      reinterpret_cast<float4 *>(p)[j] = make_float4(x.v[4 * j], x.v[4 * j + 1], x.v[4 * j + 2], x.v[4 * j + 3]);
+  } else if constexpr (N == 8) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = pack2<TO>(x.v[2 * j], x.v[2 * j + 1]);
+    *reinterpret_cast<u32x4 *>(p) = w;
+  } else {
+    static_assert(N == 4, "4 or 8 elements");
+    *reinterpret_cast<u32x2 *>(p) = u32x2{pack2<TO>(x.v[0], x.v[1]), pack2<TO>(x.v[2], x.v[3])};
+  }
 }
 
 // Workgroup x of a per-(chunk, query head) grid -> (hq, c); false for the
@@ -177,7 +184,10 @@ __global__ __launch_bounds__(256) void k_chunk_scan(float *__restrict__ csum,
   const int grp = threadIdx.x >> 5;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
-  const int nch = (int)((eos - bos + CHUNK - 1) / CHUNK);
+  // at most NCmax chunks per segment have workspace slots (a max_seqlen below
+  // the true length leaves the rest of the segment unprocessed, never out of
+  // bounds)
+  const int nch = min((int)((eos - bos + CHUNK - 1) / CHUNK), NCmax);
   const bool active = ch < KD || (ch == KD && with_gs);
   const int span = (nch + 7) / 8;
   const int cb = grp * span, ce = min(nch, cb + span);
@@ -360,13 +370,84 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   }
 }
 
-// Phase C for the stand-alone prefix: P2 = (offset + in-chunk sum) * log2(e).
+// Stand-alone prefix (the decode path's P2 and gate sums G2), accumulated
+// in double so that each stored float is the running sum rounded once:
+// decode scores reach ~1e5 on long random-walk decays, where the float error
+// of a float-accumulated scan would show in the lse.
+// Phase B in double: exclusive offsets of the chunk sums (channel KD stands
+// for g_scalar).  grid (HQ, nseg, ceil((KD+1)/32)), 256 threads = 32
+// channels x 8 chunk groups.
+template <int KD>
+__global__ __launch_bounds__(256) void k_scan_offsets_f64(const float *__restrict__ csum,
+                                                          const float *__restrict__ csum_s,
+                                                          double *__restrict__ off,
+                                                          double *__restrict__ off_s,
+                                                          const int32_t *__restrict__ cu,
+                                                          int64_t T, int HQ, int NCmax,
+                                                          int with_gs) {
+  const int hq = blockIdx.x, s = blockIdx.y;
+  const int ch = blockIdx.z * 32 + (threadIdx.x & 31);
+  const int grp = threadIdx.x >> 5;
+  int64_t bos, eos;
+  segment_bounds(s, T, cu, bos, eos);
+  const int nch = min((int)((eos - bos + CHUNK - 1) / CHUNK), NCmax);
+  const bool active = ch < KD || (ch == KD && with_gs);
+  const int span = (nch + 7) / 8;
+  const int cb = grp * span, ce = min(nch, cb + span);
+  const int64_t c0 = (int64_t)s * NCmax;
+  const float *src;
+  double *dst;
+  int64_t stride;
+  if (ch < KD) {
+    src = csum + (c0 * HQ + hq) * KD + ch;
+    dst = off + (c0 * HQ + hq) * KD + ch;
+    stride = (int64_t)HQ * KD;
+  } else {
+    src = csum_s + c0 * HQ + hq;
+    dst = off_s + c0 * HQ + hq;
+    stride = HQ;
+  }
+  double tot = 0.0;
+  if (active)
+    for (int c = cb; c < ce; c += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? src[(int64_t)(c + u) * stride] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) tot += (double)x[u];
+    }
+  __shared__ double part[8][32];
+  part[grp][threadIdx.x & 31] = tot;
+  __syncthreads();
+  if (!active) return;
+  double run = 0.0;
+  for (int q = 0; q < grp; ++q) run += part[q][threadIdx.x & 31];
+  for (int c = cb; c < ce; c += 8) {
+    float x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? src[(int64_t)(c + u) * stride] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (c + u < ce) {
+        dst[(int64_t)(c + u) * stride] = run;
+        run += (double)x[u];
+      }
+  }
+}
+
+// Phase C in double: P2 = round_to_float((offset + in-chunk sum) * log2(e)),
+// and G2 likewise for g_scalar.  grid (cg.size(), nseg), 256 threads; a
+// thread owns CPT channels of RPG consecutive rows.
 template <typename TE, int KD>
-__global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
-                                                      const float *__restrict__ off,
-                                                      float *__restrict__ P2,
-                                                      const int32_t *__restrict__ cu, int64_t T,
-                                                      int HQ, int NCmax, ChunkGrid cg) {
+__global__ __launch_bounds__(256) void k_prefix_write_f64(const TE *__restrict__ g,
+                                                          const TE *__restrict__ gs,
+                                                          const double *__restrict__ off,
+                                                          const double *__restrict__ off_s,
+                                                          float *__restrict__ P2,
+                                                          float *__restrict__ G2,
+                                                          const int32_t *__restrict__ cu,
+                                                          int64_t T, int HQ, int NCmax,
+                                                          ChunkGrid cg) {
   int hq, c;
   if (!cg.map(blockIdx.x, hq, c)) return;
   const int s = blockIdx.y;
@@ -375,24 +456,60 @@ __global__ __launch_bounds__(256) void k_prefix_write(const TE *__restrict__ g,
   const int64_t r0 = bos + (int64_t)c * CHUNK;
   if (r0 >= eos) return;
   const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
-  typedef ChunkScan<TE, KD> CS;
-  constexpr int CPT = CS::CPT;
-  const int cgi = threadIdx.x % CS::NQ, grp = threadIdx.x / CS::NQ;
+  constexpr int CPT = cpt<TE>(), NQ = KD / CPT, NG = 256 / NQ, RPG = CHUNK / NG;
+  const int cgi = threadIdx.x % NQ, grp = threadIdx.x / NQ;
   const int64_t cidx = (int64_t)s * NCmax + c;
-  const FV<CPT> base = loadv<float, CPT>(off + (cidx * HQ + hq) * KD + CPT * cgi);
-  FV<CPT> p2[CS::RPG];
-  CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
+  const double L2E = 1.4426950408889634074;
+  FV<CPT> xs[RPG];
 #pragma unroll
-  for (int i = 0; i < CS::RPG; ++i) {
-    const int r = grp * CS::RPG + i;
-    if (r < nrow) storev<float, CPT>(P2 + ((r0 + r) * HQ + hq) * KD + CPT * cgi, p2[i]);
+  for (int i = 0; i < RPG; ++i) {
+    const int r = grp * RPG + i;
+    xs[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
+  }
+  double acc[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) acc[j] = 0.0;
+#pragma unroll
+  for (int i = 0; i < RPG; ++i)
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] += (double)xs[i].v[j];
+  __shared__ double tot[NG][KD];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) tot[grp][CPT * cgi + j] = acc[j];
+  __syncthreads();
+  double base[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) base[j] = off[(cidx * HQ + hq) * KD + CPT * cgi + j];
+  for (int q = 0; q < grp; ++q)
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) base[j] += tot[q][CPT * cgi + j];
+#pragma unroll
+  for (int i = 0; i < RPG; ++i) {
+    FV<CPT> out;
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) {
+      base[j] += (double)xs[i].v[j];
+      out.v[j] = (float)(base[j] * L2E);
+    }
+    const int r = grp * RPG + i;
+    if (r < nrow) storev<float, CPT>(P2 + ((r0 + r) * HQ + hq) * KD + CPT * cgi, out);
+  }
+  if (gs != nullptr && threadIdx.x < 64) {
+    const int r = threadIdx.x;
+    double x = r < nrow ? (double)Elem<TE>::ld(gs + (r0 + r) * HQ + hq) : 0.0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const double y = __shfl_up(x, d);
+      if (r >= d) x += y;
+    }
+    if (r < nrow) G2[(r0 + r) * HQ + hq] = (float)((off_s[cidx * HQ + hq] + x) * L2E);
   }
 }
 
 // Decode cache: r_cache[c] = P2 at the chunk's last token (copied), and
-// k_tilde = k * 2^(r_cache[c] - P2) in the operand type.
+// k_tilde = k * 2^(r_cache[c] - P2) rounded to the cache type TO.
 // grid (cg.size(), B), 256 threads; each thread owns CPT channels.
-template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
+template <typename TE, int KD, typename TO>
 __global__ __launch_bounds__(256) void k_build_cache(const TE *__restrict__ k,
                                                      const float *__restrict__ P2,
                                                      TO *__restrict__ kt, float *__restrict__ rc,
@@ -429,6 +546,67 @@ __global__ __launch_bounds__(256) void k_build_cache(const TE *__restrict__ k,
   }
 }
 
+// Streaming append (one token per batch row) to a decode cache of any
+// layout.  Token t = len_b goes to chunk c = t / C.  The open chunk keeps its
+// anchor at its newest token, rounded to an integer: R_new = rint(p_new),
+// k_tilde_t = k_t * 2^(R_new - p_new), and the rows already in the chunk are
+// re-anchored by 2^(R_new - R_old) -- an exact power of two when R_old is an
+// integer too (always, except for a chunk left open by the cache build,
+// whose anchor is a copied P2: one rounding at its first append).  Rows of
+// a full cache (len_b >= T) are left alone.
+// grid (HQ, B), 256 threads.
+template <typename TE, typename TK, int KD>
+__global__ __launch_bounds__(256) void k_cache_append(AppendProblem p) {
+  const int hq = blockIdx.x, b = blockIdx.y, HQ = (int)p.HQ, H = (int)p.H;
+  const int h = hq / (HQ / H);
+  const int t = __builtin_amdgcn_readfirstlane(max(p.seqlens[b], 0));
+  if (t >= p.T) return;
+  const int tc = t - t % CHUNK;  // first token of the open chunk
+  const int nold = t - tc;
+  const int64_t row0 = uniform64(cache_row(p.block_table, p.max_blocks, (int)p.page_size,
+                                           (int)p.num_pages, p.T, b, tc));
+  const int64_t anchor = p.block_table != nullptr ? row0 / CHUNK
+                                                  : (int64_t)b * ((p.T + CHUNK - 1) / CHUNK) + tc / CHUNK;
+  __shared__ float fac[KD];
+  const float *pn = p.p_new + ((int64_t)b * HQ + hq) * KD;
+  float *rcp = p.rc + (anchor * HQ + hq) * KD;
+  TK *kt = static_cast<TK *>(p.kt);
+  for (int n = threadIdx.x; n < KD; n += 256) {
+    const float rn = rintf(pn[n]);
+    float f = 1.f;
+    if (nold > 0) {
+      const float d = rn - rcp[n];
+      f = d == rintf(d) ? __builtin_amdgcn_ldexpf(1.f, (int)d) : exp2f(d);
+    }
+    fac[n] = f;
+    const float kn = Elem<TE>::ld(static_cast<const TE *>(p.k) + ((int64_t)b * H + h) * KD + n);
+    Elem<TK>::st(kt + ((row0 + nold) * HQ + hq) * KD + n, kn * exp2f(rn - pn[n]));
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < nold * KD; x += 256) {
+    const int r = x / KD, n = x % KD;
+    TK *e = kt + ((row0 + r) * HQ + hq) * KD + n;
+    Elem<TK>::st(e, Elem<TK>::ld(e) * fac[n]);
+  }
+  __syncthreads();  // every thread has read its old anchors
+  for (int n = threadIdx.x; n < KD; n += 256) rcp[n] = rintf(pn[n]);
+  if (p.gs_cache != nullptr && threadIdx.x == 0)
+    p.gs_cache[(row0 + nold) * HQ + hq] = p.gs_new[(int64_t)b * HQ + hq];
+  if (hq % (HQ / H) == 0)
+    for (int n = threadIdx.x; n < p.V; n += 256)
+      static_cast<TE *>(p.vc)[((row0 + nold) * H + h) * p.V + n] =
+          static_cast<const TE *>(p.v)[((int64_t)b * H + h) * p.V + n];
+}
+
+// After an append: every row that had room holds one more token.
+__global__ __launch_bounds__(256) void k_seqlens_advance(int32_t *__restrict__ seqlens,
+                                                         int64_t B, int64_t T) {
+  for (int64_t b = blockIdx.x * 256 + threadIdx.x; b < B; b += (int64_t)gridDim.x * 256) {
+    const int L = max(seqlens[b], 0);
+    seqlens[b] = L < T ? L + 1 : L;
+  }
+}
+
 template <typename TE, int KD>
 hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
   typedef typename OperandOf<TE>::type TO;
@@ -452,22 +630,50 @@ hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStrea
 }
 
 template <typename TE, int KD>
-hipError_t prefix_log2_t(const void *g, float *P2, const int32_t *cu, int64_t T, int64_t HQ,
-                         int64_t nseg, int64_t maxlen, float *csum, hipStream_t st) {
+hipError_t prefix_log2_t(const void *g, const void *gs, float *P2, float *G2, const int32_t *cu,
+                         int64_t T, int64_t HQ, int64_t nseg, int64_t maxlen, void *ws,
+                         hipStream_t st) {
   const int NCmax = (int)((maxlen + CHUNK - 1) / CHUNK);
+  const int64_t n = nseg * NCmax;
+  // workspace: float chunk sums [n, HQ, K] and [n, HQ], then double offsets
+  float *csum = static_cast<float *>(ws);
+  float *csum_s = csum + n * HQ * KD;
+  double *off = reinterpret_cast<double *>(static_cast<char *>(ws) + ((sizeof(float) * n * HQ * (KD + 1) + 255) & ~size_t(255)));
+  double *off_s = off + n * HQ * KD;
   const ChunkGrid cgA = chunk_grid(HQ, 1, NCmax, nseg);
   const dim3 gridA(cgA.size(), (unsigned)nseg);
+  const TE *gsp = static_cast<const TE *>(gs);
   hipLaunchKernelGGL((k_chunk_sums<TE, KD>), gridA, dim3(256), 0, st,
-                     static_cast<const TE *>(g), (const TE *)nullptr, csum, (float *)nullptr, cu,
-                     T, (int)HQ, NCmax, cgA);
-  // The anchors of phase B are not needed here; they go to the upper half of
-  // the workspace, which prefix_workspace_layout reserves for them.
-  float *anch = csum + (int64_t)nseg * NCmax * HQ * KD;
-  const dim3 gridB((unsigned)HQ, (unsigned)nseg, KD / 32);
-  hipLaunchKernelGGL((k_chunk_scan<KD>), gridB, dim3(256), 0, st, csum, anch, (float *)nullptr,
-                     cu, T, (int)HQ, NCmax, 0);
-  hipLaunchKernelGGL((k_prefix_write<TE, KD>), gridA, dim3(256), 0, st,
-                     static_cast<const TE *>(g), csum, P2, cu, T, (int)HQ, NCmax, cgA);
+                     static_cast<const TE *>(g), gsp, csum, csum_s, cu, T, (int)HQ, NCmax, cgA);
+  const dim3 gridB((unsigned)HQ, (unsigned)nseg, (KD + 1 + 31) / 32);
+  hipLaunchKernelGGL((k_scan_offsets_f64<KD>), gridB, dim3(256), 0, st, csum, csum_s, off, off_s,
+                     cu, T, (int)HQ, NCmax, gs != nullptr ? 1 : 0);
+  hipLaunchKernelGGL((k_prefix_write_f64<TE, KD>), gridA, dim3(256), 0, st,
+                     static_cast<const TE *>(g), gsp, off, off_s, P2, G2, cu, T, (int)HQ, NCmax,
+                     cgA);
+  return hipGetLastError();
+}
+
+template <typename TE, typename TK, int KD>
+hipError_t build_cache_t(const void *k, const float *P2, void *kt, float *rc, int64_t B, int64_t T,
+                         int64_t HQ, int64_t H, hipStream_t st) {
+  const int NC = (int)((T + CHUNK - 1) / CHUNK);
+  const ChunkGrid cg = chunk_grid(H, HQ / H, NC, B);
+  const dim3 grid(cg.size(), (unsigned)B);
+  hipLaunchKernelGGL((k_build_cache<TE, KD, TK>), grid, dim3(256), 0, st,
+                     static_cast<const TE *>(k), P2, static_cast<TK *>(kt), rc, T, (int)HQ,
+                     (int)H, NC, cg);
+  return hipGetLastError();
+}
+
+template <typename TE, typename TK>
+hipError_t append_t(const AppendProblem &p, hipStream_t st) {
+  if (p.K == 64)
+    hipLaunchKernelGGL((k_cache_append<TE, TK, 64>), dim3((unsigned)p.HQ, (unsigned)p.B), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_cache_append<TE, TK, 128>), dim3((unsigned)p.HQ, (unsigned)p.B), dim3(256), 0, st, p);
+  const unsigned nb = (unsigned)((p.B + 255) / 256 < 1024 ? (p.B + 255) / 256 : 1024);
+  hipLaunchKernelGGL(k_seqlens_advance, dim3(nb), dim3(256), 0, st, p.seqlens, p.B, p.T);
   return hipGetLastError();
 }
 
@@ -502,11 +708,9 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
   return off;
 }
 
-size_t prefix_workspace_layout(int64_t nseg, int64_t maxlen, int64_t HQ, int64_t K, float **csum,
-                               char *base) {
-  const int64_t NCmax = (maxlen + CHUNK - 1) / CHUNK;
-  if (csum) *csum = reinterpret_cast<float *>(base);
-  return align256(2 * sizeof(float) * nseg * NCmax * HQ * K);
+size_t prefix_workspace_layout(int64_t nseg, int64_t maxlen, int64_t HQ, int64_t K) {
+  const int64_t n = nseg * ((maxlen + CHUNK - 1) / CHUNK);
+  return align256(sizeof(float) * n * HQ * (K + 1)) + align256(sizeof(double) * n * HQ * (K + 1));
 }
 
 hipError_t launch_prefix_phases(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
@@ -516,42 +720,46 @@ hipError_t launch_prefix_phases(const FwdProblem &p, const FwdWorkspace &ws, hip
   return p.K == 64 ? prefix_phases_t<float, 64>(p, ws, st) : prefix_phases_t<float, 128>(p, ws, st);
 }
 
-hipError_t launch_prefix_log2(const void *g, float *P2, const int32_t *cu, int64_t T, int64_t HQ,
-                              int64_t K, int64_t nseg, int64_t maxlen, int dtype, float *csum,
-                              hipStream_t st) {
-  if (dtype == 0)
-    return K == 64 ? prefix_log2_t<bf16_t, 64>(g, P2, cu, T, HQ, nseg, maxlen, csum, st)
-                   : prefix_log2_t<bf16_t, 128>(g, P2, cu, T, HQ, nseg, maxlen, csum, st);
-  return K == 64 ? prefix_log2_t<float, 64>(g, P2, cu, T, HQ, nseg, maxlen, csum, st)
-                 : prefix_log2_t<float, 128>(g, P2, cu, T, HQ, nseg, maxlen, csum, st);
+hipError_t launch_prefix_log2(const void *g, const void *gs, float *P2, float *G2,
+                              const int32_t *cu, int64_t T, int64_t HQ, int64_t K, int64_t nseg,
+                              int64_t maxlen, int dtype, void *ws, hipStream_t st) {
+  if (dtype == WA_DT_BF16)
+    return K == 64 ? prefix_log2_t<bf16_t, 64>(g, gs, P2, G2, cu, T, HQ, nseg, maxlen, ws, st)
+                   : prefix_log2_t<bf16_t, 128>(g, gs, P2, G2, cu, T, HQ, nseg, maxlen, ws, st);
+  return K == 64 ? prefix_log2_t<float, 64>(g, gs, P2, G2, cu, T, HQ, nseg, maxlen, ws, st)
+                 : prefix_log2_t<float, 128>(g, gs, P2, G2, cu, T, HQ, nseg, maxlen, ws, st);
+}
+
+template <typename TE>
+static hipError_t build_cache_te(const void *k, const float *P2, void *kt, float *rc, int64_t B,
+                                 int64_t T, int64_t HQ, int64_t H, int64_t K, int cache_dtype,
+                                 hipStream_t st) {
+  if (K == 64) {
+    if (cache_dtype == WA_DT_BF16) return build_cache_t<TE, bf16_t, 64>(k, P2, kt, rc, B, T, HQ, H, st);
+    if (cache_dtype == WA_DT_F16) return build_cache_t<TE, _Float16, 64>(k, P2, kt, rc, B, T, HQ, H, st);
+    return build_cache_t<TE, float, 64>(k, P2, kt, rc, B, T, HQ, H, st);
+  }
+  if (cache_dtype == WA_DT_BF16) return build_cache_t<TE, bf16_t, 128>(k, P2, kt, rc, B, T, HQ, H, st);
+  if (cache_dtype == WA_DT_F16) return build_cache_t<TE, _Float16, 128>(k, P2, kt, rc, B, T, HQ, H, st);
+  return build_cache_t<TE, float, 128>(k, P2, kt, rc, B, T, HQ, H, st);
 }
 
 hipError_t launch_build_cache(const void *k, const float *P2, void *kt, float *rc, int64_t B,
                               int64_t T, int64_t HQ, int64_t H, int64_t K, int dtype,
-                              hipStream_t st) {
-  const int NC = (int)((T + CHUNK - 1) / CHUNK);
-  const ChunkGrid cg = chunk_grid(H, HQ / H, NC, B);
-  const dim3 grid(cg.size(), (unsigned)B);
-  if (dtype == 0) {
-    if (K == 64)
-      hipLaunchKernelGGL((k_build_cache<bf16_t, 64>), grid, dim3(256), 0, st,
-                         static_cast<const bf16_t *>(k), P2, static_cast<_Float16 *>(kt), rc, T,
-                         (int)HQ, (int)H, NC, cg);
-    else
-      hipLaunchKernelGGL((k_build_cache<bf16_t, 128>), grid, dim3(256), 0, st,
-                         static_cast<const bf16_t *>(k), P2, static_cast<_Float16 *>(kt), rc, T,
-                         (int)HQ, (int)H, NC, cg);
-  } else {
-    if (K == 64)
-      hipLaunchKernelGGL((k_build_cache<float, 64>), grid, dim3(256), 0, st,
-                         static_cast<const float *>(k), P2, static_cast<float *>(kt), rc, T,
-                         (int)HQ, (int)H, NC, cg);
-    else
-      hipLaunchKernelGGL((k_build_cache<float, 128>), grid, dim3(256), 0, st,
-                         static_cast<const float *>(k), P2, static_cast<float *>(kt), rc, T,
-                         (int)HQ, (int)H, NC, cg);
+                              int cache_dtype, hipStream_t st) {
+  if (dtype == WA_DT_BF16) return build_cache_te<bf16_t>(k, P2, kt, rc, B, T, HQ, H, K, cache_dtype, st);
+  return build_cache_te<float>(k, P2, kt, rc, B, T, HQ, H, K, cache_dtype, st);
+}
+
+hipError_t launch_cache_append(const AppendProblem &p, hipStream_t st) {
+  if (p.dtype == WA_DT_BF16) {
+    if (p.cache_dtype == WA_DT_BF16) return append_t<bf16_t, bf16_t>(p, st);
+    if (p.cache_dtype == WA_DT_F16) return append_t<bf16_t, _Float16>(p, st);
+    return append_t<bf16_t, float>(p, st);
   }
-  return hipGetLastError();
+  if (p.cache_dtype == WA_DT_BF16) return append_t<float, bf16_t>(p, st);
+  if (p.cache_dtype == WA_DT_F16) return append_t<float, _Float16>(p, st);
+  return append_t<float, float>(p, st);
 }
 
 }  // namespace wa

@@ -139,28 +139,49 @@ def make_prefill(cfg: Prefill, device="cpu", seed: Optional[int] = None) -> dict
     return out
 
 
-def make_decode(cfg: Decode, device="cpu", seed: Optional[int] = None) -> dict:
-    """Inputs for the decode workload: k, v, g over the cache and the newest query.
+def decode_row(cfg: Decode, b: int) -> dict:
+    """Batch row b of a decode workload, drawn on the CPU with its own
+    generator (seed * 100003 + b), in the order k, v, g, q: any row can be
+    drawn alone, identically on every machine.
 
-    Keys: k [B,T_kv,H,K], v [B,T_kv,H,V], g [B,T_kv,HQ,K], q [B,1,HQ,K] (cfg.dtype),
-    sink_bias [HQ] float32 or None, scale.  Drawn with a generator on
-    ``device`` (the 32K-token cache is too large to draw quickly on the CPU);
-    the same device type and seed give the same values.
+    Keys: k [1,T_kv,H,K], v [1,T_kv,H,V], g [1,T_kv,HQ,K], q [1,1,HQ,K] in
+    cfg.dtype."""
+    gen = _gen("cpu", cfg.seed * 100003 + b)
+    f32, dt, T = torch.float32, cfg.dtype, cfg.T_kv
+    k = torch.randn(1, T, cfg.H, cfg.K, generator=gen, dtype=f32).to(dt)
+    v = torch.randn(1, T, cfg.H, cfg.V, generator=gen, dtype=f32).to(dt)
+    g = (torch.randn(1, T, cfg.HQ, cfg.K, generator=gen, dtype=f32) * cfg.g_std).to(dt)
+    q = torch.randn(1, 1, cfg.HQ, cfg.K, generator=gen, dtype=f32).to(dt)
+    return dict(k=k, v=v, g=g, q=q)
+
+
+def decode_sink(cfg: Decode):
+    """sink_bias of a decode workload (float32 [HQ], seed * 100003 - 1), or None."""
+    if not cfg.sink:
+        return None
+    return torch.randn(cfg.HQ, generator=_gen("cpu", cfg.seed * 100003 - 1), dtype=torch.float32)
+
+
+def make_decode(cfg: Decode, device="cpu", threads: int = 16) -> dict:
+    """Inputs for a decode workload: k, v, g over the cache and the newest query.
+
+    Keys: k [B,T_kv,H,K], v [B,T_kv,H,V], g [B,T_kv,HQ,K], q [B,1,HQ,K]
+    (cfg.dtype) on ``device``, sink_bias [HQ] float32 or None, scale.  Every
+    batch row is ``decode_row(cfg, b)`` (rows are drawn in parallel host
+    threads, each with its own generator, and copied to ``device`` as they
+    finish).
     """
-    seed = cfg.seed if seed is None else seed
-    gen = _gen(device, seed)
-    f32 = torch.float32
-    B, T = cfg.B, cfg.T_kv
-    dt = cfg.dtype
-
-    def rn(*shape):
-        return torch.randn(*shape, generator=gen, dtype=f32, device=device)
-
-    k = rn(B, T, cfg.H, cfg.K).to(dt)
-    v = rn(B, T, cfg.H, cfg.V).to(dt)
-    g = torch.empty(B, T, cfg.HQ, cfg.K, dtype=dt, device=device)
-    for b in range(B):  # per batch row, to bound the float32 staging buffer
-        g[b] = (rn(T, cfg.HQ, cfg.K) * cfg.g_std).to(dt)
-    q = rn(B, 1, cfg.HQ, cfg.K).to(dt)
-    sink = rn(cfg.HQ) if cfg.sink else None
-    return dict(k=k, v=v, g=g, q=q, sink_bias=sink, scale=cfg.K ** -0.5)
+    from concurrent.futures import ThreadPoolExecutor
+    B, T, dt = cfg.B, cfg.T_kv, cfg.dtype
+    out = dict(k=torch.empty(B, T, cfg.H, cfg.K, dtype=dt, device=device),
+               v=torch.empty(B, T, cfg.H, cfg.V, dtype=dt, device=device),
+               g=torch.empty(B, T, cfg.HQ, cfg.K, dtype=dt, device=device),
+               q=torch.empty(B, 1, cfg.HQ, cfg.K, dtype=dt, device=device))
+    with ThreadPoolExecutor(max_workers=max(1, min(threads, B))) as ex:
+        for b, row in enumerate(ex.map(lambda i: decode_row(cfg, i), range(B))):
+            for key in ("k", "v", "g", "q"):
+                out[key][b:b + 1].copy_(row[key])
+    sink = decode_sink(cfg)
+    out["sink_bias"] = None if sink is None else sink.to(device)
+    out["scale"] = cfg.K ** -0.5
+    return out

@@ -48,10 +48,16 @@ enum {
   WA_WORKSPACE_TOO_SMALL = 4 /* workspace_bytes below the matching *_workspace_bytes() */
 };
 
-/* Element types of q, k, v, g, g_scalar, o (README "Features": BF16 and FP32
- * inputs).  Statistics (P2, anchors, p_curr, r_cache, sink_bias, lse) are
- * always float32; the decode cache k_tilde is IEEE half for WA_BF16. */
-enum { WA_BF16 = 0, WA_F32 = 1 };
+/* Element types.  q, k, v, g, g_scalar, o are WA_BF16 or WA_F32 (README
+ * "Features": BF16 and FP32 inputs).  The decode cache k_tilde is any of the
+ * three (the `cache_dtype` arguments): WA_BF16 is k's own type (the README's
+ * cache), WA_F16 has 3 more mantissa bits in the same 2 bytes, WA_F32 keeps
+ * 24 bits -- the format that holds long random-walk decays, whose decode
+ * scores reach ~1e5 and whose softmax turns on score differences of a few
+ * units (a 32K-token cache with g ~ 0.02 N(0,1): 16-bit caches move some
+ * outputs by 0.07-3.5, float32 by < 2e-3).  Statistics (P2, G2, anchors,
+ * p_curr, r_cache, gate caches, sink_bias, lse) are always float32. */
+enum { WA_BF16 = 0, WA_F32 = 1, WA_F16 = 2 };
 
 /* Message for the last failing call on this host thread ("" if none). */
 const char *wall_attn_last_error(void);
@@ -67,7 +73,10 @@ size_t wall_attn_fwd_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t H
 
 /*
  * Prefill / training forward (README "Usage": wall_attn(q, k, v, g, scale,
- * g_scalar, sink_bias, window_size, cu_seqlens) -> o).
+ * g_scalar, sink_bias, window_size, cu_seqlens) -> o).  With cu_seqlens, a
+ * sequence longer than max_seqlen is processed only up to its first
+ * ceil(max_seqlen/64)*64 tokens and its later rows of o and lse are not
+ * written (nothing is read or written out of bounds).
  *
  *   q, k, v, g     inputs in `dtype`, shapes as in the notation above.
  *   g_scalar       [B,T,HQ] in `dtype`, FoX-style additive gate; NULL = none.
@@ -91,7 +100,8 @@ size_t wall_attn_fwd_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t H
  * cu_seqlens with B != 1, non-positive sizes, NULL required pointers or
  * misaligned pointers; UNSUPPORTED for other K, V or dtype, and for a launch
  * grid beyond the hardware's (segments or HQ above 65535, or
- * HQ*(ceil(max_seqlen/64)+8)*segments >= 2^31, segments = num_seqs or B);
+ * HQ*(ceil(max_seqlen/64)+8)*segments*256 >= 2^32 work-items, segments =
+ * num_seqs or B);
  * WORKSPACE_TOO_SMALL; HIP_ERROR if a launch fails.
  */
 int wall_attn_fwd(const void *q, const void *k, const void *v, const void *g,
@@ -143,12 +153,17 @@ size_t wall_attn_prefix_log2_workspace_bytes(int64_t B, int64_t T, int64_t HQ, i
  * the chunked global cumulative sum of g scaled by 1/ln 2):
  *   P2[t,hq,n] = (1/ln 2) * sum_{u=bos..t} g[u,hq,n], restarting at every
  * sequence start bos.  g [B,T,HQ,K] in `dtype` -> P2 [B,T,HQ,K] float32.
- * cu_seqlens / num_seqs / max_seqlen as in wall_attn_fwd.
+ * Optionally the same for the scalar gate: g_scalar [B,T,HQ] -> G2 [B,T,HQ]
+ * float32 (both NULL or both given; G2 feeds the gate cache of
+ * wall_attn_decode_ext).  The sums are accumulated in double and each output
+ * is rounded to float once.  cu_seqlens / num_seqs / max_seqlen as in
+ * wall_attn_fwd; with cu_seqlens, at most ceil(max_seqlen/64) chunks of a
+ * sequence are processed (tokens beyond max_seqlen are not written).
  */
-int wall_attn_prefix_log2(const void *g, float *P2, int64_t B, int64_t T, int64_t HQ, int64_t K,
-                          const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
-                          int dtype, void *workspace, size_t workspace_bytes,
-                          struct ihipStream_t *stream);
+int wall_attn_prefix_log2(const void *g, const void *g_scalar, float *P2, float *G2, int64_t B,
+                          int64_t T, int64_t HQ, int64_t K, const int32_t *cu_seqlens,
+                          int64_t num_seqs, int64_t max_seqlen, int dtype, void *workspace,
+                          size_t workspace_bytes, struct ihipStream_t *stream);
 
 /*
  * Decode cache build (README "Decode": build_wall_kv_cache(k, P, chunk_size)).
@@ -157,20 +172,19 @@ int wall_attn_prefix_log2(const void *g, float *P2, int64_t B, int64_t T, int64_
  * and the decay is folded into the keys, one copy per query head:
  *   k_tilde[b,j,hq,n] = k[b,j,h(hq),n] * 2^(r_cache[b,c(j),hq,n] - P2[b,j,hq,n]).
  *   k [B,T_kv,H,K] (dtype), P2 [B,T_kv,HQ,K] float32
- *   -> k_tilde [B,T_kv,HQ,K] rounded to nearest even: IEEE half for WA_BF16
- *      inputs (same size as bfloat16 with 3 more mantissa bits; every stored
- *      factor 2^(R_c - P2[j]) spans at most one chunk's decay), float32 for
- *      WA_F32;  r_cache [B,ceil(T_kv/C),HQ,K] float32.
- * Supported: chunk_size == 64, K in {64, 128}; B <= 65535 and
- * HQ*(ceil(T_kv/64)+8)*B < 2^31 (launch grid); for WA_BF16 also
- * T_kv*HQ*K*2 < 2^31 (the forward's per-sequence limit, which the decode
- * shares); else UNSUPPORTED.
+ *   -> k_tilde [B,T_kv,HQ,K] in cache_dtype (WA_BF16, WA_F16 or WA_F32),
+ *      rounded to nearest even;  r_cache [B,ceil(T_kv/C),HQ,K] float32.
+ * Supported: chunk_size == 64, K in {64, 128}; B, HQ <= 65535,
+ * T_kv < 2^31 - 64, HQ*(ceil(T_kv/64)+8)*256 < 2^32; else UNSUPPORTED.
  */
 int wall_attn_build_kv_cache(const void *k, const float *P2, void *k_tilde, float *r_cache,
                              int64_t B, int64_t T_kv, int64_t HQ, int64_t H, int64_t K,
-                             int64_t chunk_size, int dtype, struct ihipStream_t *stream);
+                             int64_t chunk_size, int dtype, int cache_dtype,
+                             struct ihipStream_t *stream);
 
-/* Bytes of device workspace wall_attn_decode needs (split partials). */
+/* Bytes of device workspace wall_attn_decode and wall_attn_decode_ext need
+ * (split partials); T_kv is the cache's rows per batch row (paged: the
+ * capacity max_blocks*page_size).  0 on bad arguments. */
 size_t wall_attn_decode_workspace_bytes(int64_t B, int64_t T_kv, int64_t HQ, int64_t H, int64_t K,
                                         int64_t V, int64_t chunk_size);
 
@@ -184,19 +198,84 @@ size_t wall_attn_decode_workspace_bytes(int64_t B, int64_t T_kv, int64_t HQ, int
  * weighted sum of v.  This equals the last row of wall_attn_fwd over the
  * same tokens (no window, no g_scalar).
  *   q [B,1,HQ,K] (dtype), v [B,T_kv,H,V] (dtype), p_curr [B,1,HQ,K] float32
- *   (P2 at the newest token), k_tilde (IEEE half for WA_BF16, float32 for
- *   WA_F32) and r_cache as built above,
+ *   (P2 at the newest token), k_tilde [B,T_kv,HQ,K] (cache_dtype) and
+ *   r_cache [B,ceil(T_kv/C),HQ,K] float32 (any anchors: they cancel),
  *   sink_bias [HQ] float32 or NULL -> o [B,1,HQ,V] (dtype),
  *   lse [B,1,HQ] float32 natural log, or NULL.
- * Supported: chunk_size == 64, K and V in {64, 128}; T_kv*HQ*K times the
- * k_tilde element size (2 or 4 bytes) < 2^31 (one batch row of the cache
- * addressed with 32-bit offsets), else UNSUPPORTED.
+ *   workspace: at least wall_attn_decode_workspace_bytes(); its contents are
+ *   scratch (split partials), overwritten by every call.
+ * Supported: chunk_size == 64, K and V in {64, 128}; B, HQ <= 65535;
+ * T_kv < 2^31 - 64; 64*HQ*K*4 and 64*H*V*4 < 2^31; B*HQ*128 < 2^32; else
+ * UNSUPPORTED.
  */
 int wall_attn_decode(const void *q, const void *v, const float *p_curr, const void *k_tilde,
                      const float *r_cache, const float *sink_bias, void *o, float *lse,
                      int64_t B, int64_t T_kv, int64_t HQ, int64_t H, int64_t K, int64_t V,
-                     int64_t chunk_size, float scale, int dtype,
+                     int64_t chunk_size, float scale, int dtype, int cache_dtype,
                      void *workspace, size_t workspace_bytes, struct ihipStream_t *stream);
+
+/*
+ * Decode with the serving options (README "Decode" and "Usage"; the
+ * FlexAttention article's decode offset, sliding window and logical-to-
+ * physical page table; the FlagAttention overview's paged decoding).  As
+ * wall_attn_decode, plus (each may be left out with NULL / 0):
+ *   cache_seqlens  int32 [B]: row b holds len_b cached tokens and its query
+ *                  sits at position len_b - 1 (NULL: every row holds T_kv).
+ *                  Values are clamped into [0, capacity]; a row with
+ *                  len_b = 0 gets o = 0 and lse = sink_bias (or -inf).
+ *   window_size    > 0: only keys j with len_b - 1 - j < window_size count
+ *                  (the forward's window rule); 0: none.
+ *   gate_cache     float32 running sums of g_scalar in log2 units per cached
+ *                  token ([B,T_kv,HQ], or the page layout below) and
+ *   gate_curr      float32 [B,1,HQ] the same at the query: the score gains
+ *                  (gate_curr - gate_cache[j]) * ln 2, the forward's
+ *                  Gs[i] - Gs[j].  Both NULL or both given.
+ *   block_table    int32 [B, max_blocks]: logical page p of row b lives in
+ *                  physical page block_table[b*max_blocks + p] of pools
+ *                  k_tilde [num_pages, page_size, HQ, K], v [num_pages,
+ *                  page_size, H, V], r_cache [num_pages, page_size/64, HQ, K]
+ *                  and gate_cache [num_pages, page_size, HQ]; page_size a
+ *                  multiple of 64; the capacity is max_blocks*page_size and
+ *                  T_kv is ignored.  Entries outside [0, num_pages) are
+ *                  clamped (such rows give undefined values, but no access
+ *                  leaves the pools).  NULL: contiguous [B, T_kv] rows.
+ * Errors: as wall_attn_decode; INVALID_ARG for a negative window_size, a
+ * gate pointer without the other, or bad page arguments.
+ */
+int wall_attn_decode_ext(const void *q, const void *v, const float *p_curr, const void *k_tilde,
+                         const float *r_cache, const float *sink_bias, const float *gate_cache,
+                         const float *gate_curr, void *o, float *lse, int64_t B, int64_t T_kv,
+                         int64_t HQ, int64_t H, int64_t K, int64_t V, int64_t chunk_size,
+                         float scale, int dtype, int cache_dtype, const int32_t *cache_seqlens,
+                         int64_t window_size, const int32_t *block_table, int64_t max_blocks,
+                         int64_t page_size, int64_t num_pages, void *workspace,
+                         size_t workspace_bytes, struct ihipStream_t *stream);
+
+/*
+ * Streaming append (README "Decode" and "Tests": the sequential-append
+ * serving loop that reproduces the forward token by token).  For every batch
+ * row b with len_b = cache_seqlens[b] < capacity, the new token goes to
+ * position t = len_b:
+ *   k_tilde[t] = k_new * 2^(R - p_new), R = rint(p_new) per channel,
+ *   v_cache[t] = v_new,  gate_cache[t] = gate_new (if given),
+ * the open chunk c = t/64 takes R as its anchor (r_cache[c] = R: the chunk
+ * stays anchored at its newest token, rounded to an integer) and its rows
+ * already cached are re-anchored, k_tilde[j] *= 2^(R - R_old) (an exact
+ * power of two when R_old is an integer, as every anchor written here is);
+ * then cache_seqlens[b] += 1.  Rows already at capacity are left unchanged.
+ *   k_new [B,1,H,K], v_new [B,1,H,V] (dtype); p_new [B,1,HQ,K] float32 (P2 at
+ *   the new token); gate_new [B,1,HQ] float32 or NULL (G2 at the new token);
+ *   caches in the layouts of wall_attn_decode_ext (contiguous [B,T_kv,...]
+ *   or paged through block_table, whose page for position t must be set).
+ * Errors: as wall_attn_decode_ext.
+ */
+int wall_attn_cache_append(const void *k_new, const void *v_new, const float *p_new,
+                           const float *gate_new, void *k_tilde, void *v_cache, float *r_cache,
+                           float *gate_cache, int32_t *cache_seqlens, int64_t B, int64_t T_kv,
+                           int64_t HQ, int64_t H, int64_t K, int64_t V, int64_t chunk_size,
+                           int dtype, int cache_dtype, const int32_t *block_table,
+                           int64_t max_blocks, int64_t page_size, int64_t num_pages,
+                           struct ihipStream_t *stream);
 
 #ifdef __cplusplus
 }

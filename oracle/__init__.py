@@ -53,6 +53,9 @@ def _load():
         lib.oracle_build_kv_cache.restype = ctypes.c_int
         lib.oracle_decode_cache.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, D, P, P]
         lib.oracle_decode_cache.restype = ctypes.c_int
+        lib.oracle_decode_cache_ext.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                                D, P, P]
+        lib.oracle_decode_cache_ext.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -178,6 +181,35 @@ def decode(q, v, p_curr, k_tilde, r_cache, sink_bias=None, scale=None, cache_chu
                                     _ptr(o), _ptr(lse))
     if r != 0:
         raise ValueError("oracle_decode_cache: bad arguments")
+    o = o.reshape(B, 1, HQ, V)
+    lse = lse.reshape(B, 1, HQ)
+    return (o, lse) if return_lse else o
+
+
+def decode_ext(q, v, p_curr, k_tilde, r_cache, sink_bias=None, scale=None, cache_chunk_size=64,
+               gate_cache=None, gate_curr=None, cache_seqlens=None, window_size=None,
+               return_lse=False):
+    """Decode over the cache with per-row lengths, a window and the gate cache
+    (README "Decode" formula, the FlexAttention window rule, the forward's
+    gate term): o [B,1,HQ,V].  Caches are contiguous [B,T,...] arrays;
+    gate_cache [B,T,HQ] and gate_curr [B,1,HQ] are running sums of g_scalar
+    in log2 units; cache_seqlens int [B]."""
+    q, v, p_curr = _f32(q), _f32(v), _f32(p_curr)
+    k_tilde, r_cache, sink = _f32(k_tilde), _f32(r_cache), _f32(sink_bias)
+    gc, gq, lens = _f32(gate_cache), _f32(gate_curr), _i32(cache_seqlens)
+    B, T, H, V = v.shape
+    HQ, K = q.shape[2], q.shape[3]
+    if scale is None:
+        scale = K ** -0.5
+    W = 0 if window_size is None else int(window_size)
+    o = np.zeros((B, HQ, V), dtype=np.float64)
+    lse = np.zeros((B, HQ), dtype=np.float64)
+    r = _load().oracle_decode_cache_ext(_ptr(q), _ptr(v), _ptr(p_curr), _ptr(k_tilde),
+                                        _ptr(r_cache), _ptr(sink), _ptr(gc), _ptr(gq), _ptr(lens),
+                                        W, B, T, HQ, H, K, V, cache_chunk_size, float(scale),
+                                        _ptr(o), _ptr(lse))
+    if r != 0:
+        raise ValueError("oracle_decode_cache_ext: bad arguments")
     o = o.reshape(B, 1, HQ, V)
     lse = lse.reshape(B, 1, HQ)
     return (o, lse) if return_lse else o

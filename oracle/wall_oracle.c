@@ -296,3 +296,77 @@ int oracle_decode_cache(const float *q, const float *v, const float *p_curr, con
   }
   return 0;
 }
+
+/*
+ * Decode over a pre-rescaled cache with the serving options (README "Decode"
+ * formula; the window rule of the FlexAttention article, section "score_mod
+ * and mask_mod"; the gate is the forward's Gs[i] - Gs[j] of README "Usage").
+ * Row b holds lens[b] cached tokens (lens NULL: all T) and its query sits at
+ * position i = lens[b] - 1; key j counts if j < lens[b] and (W <= 0 or
+ * i - j < W).  With a gate cache (running sums of g_scalar in log2 units)
+ * the score of key j gains (gate_curr[b,hq] - gate_cache[b,j,hq]) * ln 2:
+ *   s_j = scale * sum_n q[n] 2^(p_curr[n] - r_cache[c(j),n]) k_tilde[j,n]
+ *         + (gate_curr - gate_cache[j]) * ln 2
+ * then the softmax over the counted keys (and the optional sink logit).  A
+ * row with no counted key gets o = 0 and lse = sink (or -inf).
+ *   q [B,HQ,K], v [B,T,H,V], p_curr [B,HQ,K], k_tilde [B,T,HQ,K],
+ *   r_cache [B,ceil(T/C),HQ,K], sink [HQ] or NULL, gate_cache [B,T,HQ] and
+ *   gate_curr [B,HQ] or NULL, lens [B] or NULL -> o [B,HQ,V], lse [B,HQ]
+ */
+int oracle_decode_cache_ext(const float *q, const float *v, const float *p_curr,
+                            const float *k_tilde, const float *r_cache, const float *sink,
+                            const float *gate_cache, const float *gate_curr, const int32_t *lens,
+                            int64_t window, int64_t B, int64_t T, int64_t HQ, int64_t H,
+                            int64_t K, int64_t V, int64_t C, double scale, double *o,
+                            double *lse) {
+  if (H <= 0 || HQ % H != 0 || C <= 0) return -1;
+  int64_t group = HQ / H;
+  int64_t nc = (T + C - 1) / C;
+  #pragma omp parallel
+  {
+    double *sc = (double *)malloc(sizeof(double) * (size_t)T);
+    #pragma omp for collapse(2) schedule(static)
+    for (int64_t b = 0; b < B; ++b) {
+      for (int64_t hq = 0; hq < HQ; ++hq) {
+        int64_t h = hq / group;
+        int64_t L = lens ? (int64_t)lens[b] : T;
+        int64_t jlo = 0;
+        if (window > 0 && L - window > 0) jlo = L - window;
+        const float *qv = q + (b * HQ + hq) * K;
+        const float *pc = p_curr + (b * HQ + hq) * K;
+        double m = -INFINITY;
+        for (int64_t j = jlo; j < L; ++j) {
+          int64_t c = j / C;
+          const float *r = r_cache + ((b * nc + c) * HQ + hq) * K;
+          const float *kt = k_tilde + ((b * T + j) * HQ + hq) * K;
+          double dot = 0.0;
+          for (int64_t n = 0; n < K; ++n)
+            dot += (double)qv[n] * exp2((double)pc[n] - (double)r[n]) * (double)kt[n];
+          double s = scale * dot;
+          if (gate_cache)
+            s += ((double)gate_curr[b * HQ + hq] - (double)gate_cache[(b * T + j) * HQ + hq]) * log(2.0);
+          sc[j] = s;
+          if (s > m) m = s;
+        }
+        if (sink && (double)sink[hq] > m) m = (double)sink[hq];
+        double *ov = o + (b * HQ + hq) * V;
+        for (int64_t c = 0; c < V; ++c) ov[c] = 0.0;
+        if (m == -INFINITY) {
+          if (lse) lse[b * HQ + hq] = -INFINITY;
+          continue;
+        }
+        double Z = 0.0;
+        for (int64_t j = jlo; j < L; ++j) Z += exp(sc[j] - m);
+        if (sink) Z += exp((double)sink[hq] - m);
+        for (int64_t j = jlo; j < L; ++j) {
+          double w = exp(sc[j] - m) / Z;
+          const float *vj = v + ((b * T + j) * H + h) * V;
+          for (int64_t c = 0; c < V; ++c) ov[c] += w * (double)vj[c];
+        }
+        if (lse) lse[b * HQ + hq] = m + log(Z);
+      }
+    }
+    free(sc);
+  }
+  return 0;
+}

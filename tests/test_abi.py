@@ -110,21 +110,22 @@ def test_workspace_sizes(lib):
 
 def test_cache_and_decode_reject_bad_arguments(lib):
     bk = lib.wall_attn_build_kv_cache
-    assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 32, 0, None) == 2   # chunk_size
-    assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 3, 64, 64, 0, None) == 1   # HQ % H
-    assert bk(None, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 64, 0, None) == 1
-    assert bk(FAKE, FAKE, FAKE + 4, FAKE, 1, 128, 4, 2, 64, 64, 0, None) == 1
-    assert bk(FAKE, FAKE, FAKE, FAKE, 70000, 128, 4, 2, 64, 64, 1, None) == 2      # B > 65535
-    assert bk(FAKE, FAKE, FAKE, FAKE, 2, 1 << 26, 1024, 8, 64, 64, 1, None) == 2   # grid x
+    assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 32, 0, 1, None) == 2   # chunk_size
+    assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 3, 64, 64, 0, 1, None) == 1   # HQ % H
+    assert bk(None, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 64, 0, 1, None) == 1
+    assert bk(FAKE, FAKE, FAKE + 4, FAKE, 1, 128, 4, 2, 64, 64, 0, 1, None) == 1
+    assert bk(FAKE, FAKE, FAKE, FAKE, 70000, 128, 4, 2, 64, 64, 1, 1, None) == 2      # B > 65535
+    assert bk(FAKE, FAKE, FAKE, FAKE, 2, 1 << 26, 1024, 8, 64, 64, 1, 1, None) == 2   # grid x
+    assert bk(FAKE, FAKE, FAKE, FAKE, 1, 128, 4, 2, 64, 64, 0, 5, None) == 2   # cache dtype
     dec = lib.wall_attn_decode
 
     def d(**kw):
         a = dict(q=FAKE, v=FAKE, p=FAKE, kt=FAKE, r=FAKE, s=None, o=FAKE, l=None, B=2, T=256,
-                 HQ=8, H=2, K=128, V=128, C=64, scale=0.0, dt=0, ws=FAKE, wsb=1 << 40)
+                 HQ=8, H=2, K=128, V=128, C=64, scale=0.0, dt=0, ct=1, ws=FAKE, wsb=1 << 40)
         a.update(kw)
         return dec(a["q"], a["v"], a["p"], a["kt"], a["r"], a["s"], a["o"], a["l"], a["B"],
-                   a["T"], a["HQ"], a["H"], a["K"], a["V"], a["C"], a["scale"], a["dt"], a["ws"],
-                   a["wsb"], None)
+                   a["T"], a["HQ"], a["H"], a["K"], a["V"], a["C"], a["scale"], a["dt"], a["ct"],
+                   a["ws"], a["wsb"], None)
     assert d(C=128) == 2
     assert d(HQ=6, H=4) == 1
     assert d(K=80) == 2
@@ -132,7 +133,49 @@ def test_cache_and_decode_reject_bad_arguments(lib):
     assert d(o=FAKE + 2) == 1
     assert d(wsb=16) == 4
     assert d(dt=3) == 2
-    assert d(T=1 << 20, HQ=32, H=8) == 2      # one batch row of the half cache beyond 2^31 bytes
+    assert d(ct=3) == 2
+    assert d(T=1 << 31) == 2                  # 32-bit token positions
+    assert d(HQ=65536 * 2, H=2) == 2          # launch grid / 32-bit chunk offsets
+
+
+def test_decode_ext_and_append_reject_bad_arguments(lib):
+    ext = lib.wall_attn_decode_ext
+
+    def d(**kw):
+        a = dict(q=FAKE, v=FAKE, p=FAKE, kt=FAKE, r=FAKE, s=None, gc=None, gq=None, o=FAKE,
+                 l=None, B=2, T=256, HQ=8, H=2, K=128, V=128, C=64, scale=0.0, dt=0, ct=1,
+                 lens=None, W=0, bt=None, mb=0, ps=0, np_=0, ws=FAKE, wsb=1 << 40)
+        a.update(kw)
+        return ext(a["q"], a["v"], a["p"], a["kt"], a["r"], a["s"], a["gc"], a["gq"], a["o"],
+                   a["l"], a["B"], a["T"], a["HQ"], a["H"], a["K"], a["V"], a["C"], a["scale"],
+                   a["dt"], a["ct"], a["lens"], a["W"], a["bt"], a["mb"], a["ps"], a["np_"],
+                   a["ws"], a["wsb"], None)
+    assert d(W=-1) == 1                                   # negative window
+    assert d(gc=FAKE) == 1                                # gate cache without gate_curr
+    assert d(gq=FAKE) == 1
+    assert d(bt=FAKE, mb=4, ps=96, np_=8) == 1            # page size not a multiple of 64
+    assert d(bt=FAKE, mb=0, ps=128, np_=8) == 1           # no blocks
+    assert d(bt=FAKE, mb=4, ps=128, np_=0) == 1           # no pages
+    assert d(bt=FAKE + 4, mb=4, ps=128, np_=8) == 1       # misaligned table
+    assert d(lens=FAKE + 4) == 1
+    # the paged capacity max_blocks*page_size sizes the workspace
+    need = lib.wall_attn_decode_workspace_bytes(2, 4 * 128, 8, 2, 128, 128, 64)
+    assert d(bt=FAKE, mb=4, ps=128, np_=8, wsb=need - 1) == 4
+    app = lib.wall_attn_cache_append
+
+    def a(**kw):
+        x = dict(k=FAKE, v=FAKE, p=FAKE, gn=None, kt=FAKE, vc=FAKE, r=FAKE, gc=None, lens=FAKE,
+                 B=2, T=256, HQ=8, H=2, K=128, V=128, C=64, dt=0, ct=1, bt=None, mb=0, ps=0, np_=0)
+        x.update(kw)
+        return app(x["k"], x["v"], x["p"], x["gn"], x["kt"], x["vc"], x["r"], x["gc"], x["lens"],
+                   x["B"], x["T"], x["HQ"], x["H"], x["K"], x["V"], x["C"], x["dt"], x["ct"],
+                   x["bt"], x["mb"], x["ps"], x["np_"], None)
+    assert a(lens=None) == 1
+    assert a(gn=FAKE) == 1
+    assert a(C=32) == 2
+    assert a(ct=9) == 2
+    assert a(HQ=6, H=4) == 1
+    assert a(bt=FAKE, mb=2, ps=100, np_=4) == 1
 
 
 def test_python_binding_fails_loudly_without_gpu_tensors():

@@ -28,11 +28,12 @@ DEV = "cuda:0"
 
 
 def lse_tol(dtype, ref):
-    """lse carries the score rounding of the rescaled operands, which grows
-    with the score magnitude: allow the output tolerance plus a relative part
-    (2^-9 of |lse| for the half operands of bf16 inputs, 2^-18 for fp32)."""
-    rel = 2.0 ** -9 if dtype == torch.bfloat16 else 2.0 ** -18
-    return TOL[dtype] + rel * np.abs(ref)
+    """Prefill lse bound: the output bound for bf16 inputs (the scores are
+    moderate on every prefill case); for fp32 inputs 1e-4 plus the float32
+    representation of lse itself, 2^-22 |lse|."""
+    if dtype == torch.bfloat16:
+        return TOL[dtype] + 0.0 * np.abs(ref)
+    return TOL[dtype] + 2.0 ** -22 * np.abs(ref)
 
 
 @pytest.fixture(scope="module")
@@ -217,36 +218,40 @@ def boundary_rows(bos, eos, step=64, extra=()):
     return rows
 
 
-def test_config_long_8k_sampled(wa):
+def test_config_long_8k_every_row(wa):
+    """Every row of the 8K workload (8192 x 16 heads) against the oracle."""
     c = W.PREFILL_T8192_BF16
     x = W.make_prefill(c)
     o, lse = run_gpu(wa, x)
-    T = c.T
-    rng = np.random.default_rng(3)
-    rows = set(range(0, T, 509)) | set(rng.integers(0, T, 24).tolist())
-    rows |= {127, 128, 129, 4095, 4096, 8063, 8064, 8190, 8191}
-    rows = sorted(rows)
-    ro, rl = run_oracle(x, rows=rows)
-    check(o.reshape(T, c.HQ, c.V)[rows], ro, 2e-2, c.name)
-    check(lse.reshape(T, c.HQ)[rows], rl, lse_tol(c.dtype, rl), c.name + " lse")
+    ro, rl = run_oracle(x)
+    check(o, ro, 2e-2, c.name)
+    check(lse, rl, lse_tol(c.dtype, rl), c.name + " lse")
 
 
-def test_config_varlen_window_sampled(wa):
+def test_config_long_8k_deterministic(wa):
+    """Two launches of the benchmark workload give identical bits."""
+    x = W.make_prefill(W.PREFILL_T8192_BF16)
+    a, la = run_gpu(wa, x)
+    b, lb = run_gpu(wa, x)
+    assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_config_varlen_window_rows(wa):
+    """Packed varlen workload: every 4th row of every sequence plus the rows
+    around each 32-, 64- and 128-row tile boundary and the window edge."""
     c = W.VARLEN_W2048_BF16
     x = W.make_prefill(c)
     o, lse = run_gpu(wa, x)
     cu = x["cu_seqlens"].tolist()
-    rng = np.random.default_rng(4)
     rows = set()
     for s in range(len(cu) - 1):
         bos, eos = cu[s], cu[s + 1]
-        rows |= {bos, bos + 1, eos - 1, eos - 2, min(eos - 1, bos + 127), min(eos - 1, bos + 128),
-                 min(eos - 1, bos + 2047), min(eos - 1, bos + 2048), min(eos - 1, bos + 2111)}
-        rows |= set(rng.integers(bos, eos, 2).tolist())
+        rows |= set(range(bos, eos, 4))
+        rows |= boundary_rows(bos, eos, step=32, extra=(bos + 2047, bos + 2048, bos + 2049))
     rows = sorted(rows)
     ro, rl = run_oracle(x, rows=rows)
     N = o.shape[1]
-    check(o.reshape(N, c.HQ, c.V)[rows], ro, 2e-2, c.name)
+    check(o.reshape(N, c.HQ, c.V)[rows], ro, 2e-2, c.name + f" ({len(rows)} rows)")
     check(lse.reshape(N, c.HQ)[rows], rl, lse_tol(c.dtype, rl), c.name + " lse")
 
 
@@ -319,170 +324,3 @@ def test_deterministic(wa):
     assert np.array_equal(a, b) and np.array_equal(la, lb)
 
 
-# ----------------------------------------------------------------------------- decode
-
-def small_decode(B=3, T=300, HQ=8, H=2, K=128, V=128, dtype=torch.bfloat16, seed=31, sink=True):
-    c = cfg("dec", B, T, HQ, H, K, V, dtype, sink=sink, seed=seed)
-    return W.make_prefill(c)
-
-
-def test_prefix_log2_matches_oracle(wa):
-    x = small_decode(T=333)
-    P2 = wa.wall_attn_prefix_log2(x["g"].to(DEV)).cpu().numpy()
-    ref = oracle.prefix_log2(x["g"])
-    check(P2, ref, 1e-4, "prefix_log2")
-    c = cfg("dec_varlen", 1, 0, 4, 2, 64, 64, torch.bfloat16, nseq=5, len_lo=1, len_hi=200, seed=32)
-    y = W.make_prefill(c)
-    P2 = wa.wall_attn_prefix_log2(y["g"].to(DEV), cu_seqlens=y["cu_seqlens"].to(DEV)).cpu().numpy()
-    check(P2, oracle.prefix_log2(y["g"], cu_seqlens=y["cu_seqlens"]), 1e-4, "prefix_log2 varlen")
-
-
-@pytest.mark.parametrize("B,T", [(3, 300), (32, 1100)], ids=["chunk_order", "pair_order"])
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_build_cache_matches_oracle(wa, dtype, B, T):
-    # 32 x 18 chunks x 8 heads exceed the workgroups the GPU holds at once:
-    # the cache build then runs its (key/value head, chunk) pair order
-    x = small_decode(B=B, T=T, dtype=dtype)
-    P2 = torch.from_numpy(oracle.prefix_log2(x["g"]).astype(np.float32))
-    kt, rc = wa.build_wall_kv_cache(x["k"].to(DEV), P2.to(DEV), chunk_size=64)
-    rkt, rrc = oracle.build_kv_cache(x["k"], P2, chunk_size=64)
-    assert np.array_equal(rc.cpu().numpy().astype(np.float64), rrc), "anchors must copy P2"
-    assert kt.dtype == wa.cache_dtype(dtype)
-    # round-to-nearest of a float32 product whose exp2 and multiply add ~2^-22
-    rel = (2.0 ** -11 if dtype == torch.bfloat16 else 0.0) + 2.0 ** -21
-    got = kt.float().cpu().numpy().astype(np.float64)
-    # half subnormals (below 2^-14) round to a multiple of 2^-24
-    absol = 2.0 ** -25 if dtype == torch.bfloat16 else 1e-30
-    assert np.all(np.abs(got - rkt) <= rel * np.abs(rkt) + absol)
-
-
-@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-def test_decode_over_oracle_cache(wa, dtype):
-    x = small_decode(T=300, dtype=dtype, B=2, HQ=8, H=2, K=64, V=128)
-    P2 = oracle.prefix_log2(x["g"]).astype(np.float32)
-    rkt, rrc = oracle.build_kv_cache(x["k"], P2, chunk_size=64)
-    kt = torch.from_numpy(rkt).to(wa.cache_dtype(dtype))   # cache rounded on the CPU
-    rc = torch.from_numpy(rrc.astype(np.float32))
-    pc = torch.from_numpy(P2[:, -1:].copy())
-    q = x["q"][:, -1:].contiguous()
-    o, lse = wa.wall_attn_decode(q.to(DEV), x["v"].to(DEV), pc.to(DEV), kt.to(DEV), rc.to(DEV),
-                                 sink_bias=x["sink_bias"].to(DEV), scale=x["scale"])
-    ro, rl = oracle.decode(q, x["v"], pc, kt, rc, sink_bias=x["sink_bias"], scale=x["scale"],
-                           return_lse=True)
-    check(o.float().cpu().numpy(), ro, TOL[dtype], "decode over oracle cache")
-    check(lse.cpu().numpy(), rl, lse_tol(dtype, rl), "decode lse")
-
-
-@pytest.mark.parametrize("T", [1, 63, 64, 65, 300, 4096])
-def test_decode_pipeline_equals_forward_last_row(wa, T):
-    x = small_decode(T=T, B=2)
-    d = to_dev(x)
-    P = wa.wall_attn_prefix_log2(d["g"])
-    kt, rc = wa.build_wall_kv_cache(d["k"], P, chunk_size=64)
-    o, lse = wa.wall_attn_decode(d["q"][:, -1:].contiguous(), d["v"], P[:, -1:].contiguous(), kt,
-                                 rc, sink_bias=d["sink_bias"], scale=d["scale"])
-    torch.cuda.synchronize()
-    rows = [b * T + T - 1 for b in range(x["q"].shape[0])]
-    ro, rl = oracle.wall_attn(x["q"], x["k"], x["v"], x["g"], scale=x["scale"],
-                              sink_bias=x["sink_bias"], rows=rows, return_lse=True)
-    check(o[:, 0].float().cpu().numpy(), ro, 2e-2, f"decode T={T} vs oracle forward")
-    check(lse[:, 0].cpu().numpy(), rl, lse_tol(torch.bfloat16, rl), f"decode lse T={T}")
-    # and the GPU prefill's last row
-    of = wa.wall_attn(d["q"], d["k"], d["v"], d["g"], scale=d["scale"], sink_bias=d["sink_bias"])
-    check(o[:, 0].float().cpu().numpy(), of[:, -1].float().cpu().numpy(), 2e-2,
-          f"decode T={T} vs GPU prefill")
-
-
-def test_decode_streaming_matches_forward(wa):
-    """Token-by-token decode reproduces every row of the forward (README "Tests")."""
-    x = small_decode(T=150, B=1, HQ=4, H=2, K=64, V=64, seed=33)
-    d = to_dev(x)
-    ro, _ = run_oracle(x)
-    P = wa.wall_attn_prefix_log2(d["g"])
-    worst = 0.0
-    for t in range(1, 151):
-        kt, rc = wa.build_wall_kv_cache(d["k"][:, :t].contiguous(), P[:, :t].contiguous())
-        o, _ = wa.wall_attn_decode(d["q"][:, t - 1:t].contiguous(), d["v"][:, :t].contiguous(),
-                                   P[:, t - 1:t].contiguous(), kt, rc, sink_bias=d["sink_bias"],
-                                   scale=d["scale"])
-        err = np.abs(o[0, 0].float().cpu().numpy() - ro[0, t - 1]).max()
-        worst = max(worst, err)
-    print(f"streaming worst max-abs {worst:.3e}", flush=True)
-    assert worst <= 2e-2
-
-
-def test_config_decode_32k_sampled(wa):
-    """Full decode workload (B=64, T_kv=32768, HQ=32, H=8, D=128, C=64) in the benchmark's
-    launch configuration.
-
-    Kernel parity: for sampled batch rows the cache rows are replaced by an oracle-built
-    cache (fp64 prefix and rescaling, rounded to the cache dtype on the CPU) and the GPU
-    decode is compared with the oracle decoding that same cache.  The end-to-end pipeline
-    (GPU prefix, GPU cache, GPU decode) is also compared with the oracle's forward last
-    row and the error is printed: with a random-walk decay over 32K tokens the decode
-    scores reach ~1e5 and the softmax is nearly an argmax with near ties, so a 16-bit
-    cache cannot reproduce every row to 2e-2 (see the design notes); the end-to-end bound
-    is asserted on the well-conditioned T_kv <= 4096 cases above.
-    """
-    c = W.DECODE_T32768_BF16
-    x = W.make_decode(c, device=DEV)
-    P = wa.wall_attn_prefix_log2(x["g"])
-    kt, rc = wa.build_wall_kv_cache(x["k"], P, chunk_size=c.C)
-    pc = P[:, -1:].contiguous()
-    del P
-    o_e2e, _ = wa.wall_attn_decode(x["q"], x["v"], pc, kt, rc, sink_bias=x["sink_bias"],
-                                   scale=x["scale"], cache_chunk_size=c.C)
-    torch.cuda.synchronize()
-    rows = (0, 41, 63)
-    ref = {}
-    for b in rows:
-        gb = x["g"][b:b + 1].cpu()
-        P2 = oracle.prefix_log2(gb).astype(np.float32)
-        rkt, rrc = oracle.build_kv_cache(x["k"][b:b + 1].cpu(), P2, chunk_size=c.C)
-        kt_b = torch.from_numpy(rkt).to(kt.dtype)
-        rc_b = torch.from_numpy(rrc.astype(np.float32))
-        pc_b = torch.from_numpy(P2[:, -1:].copy())
-        kt[b:b + 1].copy_(kt_b.to(DEV))
-        rc[b:b + 1].copy_(rc_b.to(DEV))
-        pc[b:b + 1].copy_(pc_b.to(DEV))
-        ref[b] = oracle.decode(x["q"][b:b + 1].cpu(), x["v"][b:b + 1].cpu(), pc_b, kt_b, rc_b,
-                               sink_bias=None if x["sink_bias"] is None else x["sink_bias"].cpu(),
-                               scale=x["scale"], cache_chunk_size=c.C, return_lse=True)
-        del rkt, rrc, P2
-    o, lse = wa.wall_attn_decode(x["q"], x["v"], pc, kt, rc, sink_bias=x["sink_bias"],
-                                 scale=x["scale"], cache_chunk_size=c.C)
-    torch.cuda.synchronize()
-    for b in rows:
-        ro, rl = ref[b]
-        check(o[b:b + 1].float().cpu().numpy(), ro, 2e-2, f"decode32k kernel b={b}")
-        check(lse[b:b + 1].cpu().numpy(), rl, lse_tol(c.dtype, rl), f"decode32k kernel lse b={b}")
-    # end to end against the forward's last row: measured and printed
-    for b in rows:
-        q = torch.zeros(1, c.T_kv, c.HQ, c.K, dtype=torch.float32)
-        q[0, -1] = x["q"][b, 0].float().cpu()
-        fo = oracle.wall_attn(q, x["k"][b:b + 1].cpu(), x["v"][b:b + 1].cpu(),
-                              x["g"][b:b + 1].cpu(), scale=x["scale"],
-                              sink_bias=None if x["sink_bias"] is None else x["sink_bias"].cpu(),
-                              rows=[c.T_kv - 1])
-        err = np.abs(o_e2e[b].float().cpu().numpy() - fo).max()
-        print(f"decode32k end-to-end b={b}: max-abs err vs forward {err:.3e}", flush=True)
-        assert np.isfinite(o_e2e[b].float().cpu().numpy()).all()
-
-
-@pytest.mark.parametrize("B,T", [(4, 4096), (2, 2048)])
-def test_decode_pipeline_full_heads_equals_forward(wa, B, T):
-    """The decode workload's head layout (HQ=32, H=8, D=128) at T_kv where the problem is
-    well conditioned: GPU prefix -> cache -> decode against the oracle forward's last row."""
-    c = cfg("dec_full_heads", B, T, 32, 8, 128, 128, torch.bfloat16, seed=40 + T)
-    x = W.make_prefill(c)
-    d = to_dev(x)
-    P = wa.wall_attn_prefix_log2(d["g"])
-    kt, rc = wa.build_wall_kv_cache(d["k"], P, chunk_size=64)
-    o, lse = wa.wall_attn_decode(d["q"][:, -1:].contiguous(), d["v"], P[:, -1:].contiguous(), kt,
-                                 rc, scale=d["scale"])
-    torch.cuda.synchronize()
-    rows = [b * T + T - 1 for b in range(B)]
-    ro, rl = oracle.wall_attn(x["q"], x["k"], x["v"], x["g"], scale=x["scale"], rows=rows,
-                              return_lse=True)
-    check(o[:, 0].float().cpu().numpy(), ro, 2e-2, f"decode heads32 T={T}")
-    check(lse[:, 0].cpu().numpy(), rl, lse_tol(torch.bfloat16, rl), f"decode heads32 lse T={T}")

@@ -366,3 +366,54 @@ def test_decode_from_cache_equals_forward_last_row(sink):
     # the float32 cache and P2 round at ~1e-7 relative
     np.testing.assert_allclose(od[:, 0], o_full[:, -1], rtol=0, atol=2e-6)
     np.testing.assert_allclose(ld[:, 0], l_full[:, -1], rtol=0, atol=2e-6)
+
+
+# ---------------------------------------------------------------- decode with serving options
+
+def _cache_for(k, g, C=64):
+    P2 = oracle.prefix_log2(g).astype(np.float32)
+    kt, rc = oracle.build_kv_cache(k, P2, chunk_size=C)
+    return P2, kt.astype(np.float32), rc.astype(np.float32)
+
+
+@pytest.mark.parametrize("window", [None, 1, 37, 100])
+def test_decode_ext_window_gate_equals_forward_row(window):
+    """Decode over the cache with a window and the gate cache reproduces the
+    forward's last row with the same window and g_scalar (README "Decode" and
+    "Tests"; the forward is pinned to SDPA and closed forms above)."""
+    B, T, HQ, H, K, V = 2, 150, 4, 2, 16, 8
+    q, k, v, g = _inputs(B, T, HQ, H, K, V, seed=220, g_scale=0.1)
+    gs = _rand((B, T, HQ), 221, 0.1)
+    sb = _rand((HQ,), 222)
+    o_full, l_full = oracle.wall_attn(q, k, v, g, g_scalar=gs, sink_bias=sb, window_size=window,
+                                      return_lse=True)
+    P2, kt, rc = _cache_for(k, g)
+    G2 = (np.cumsum(gs.numpy().astype(np.float64), axis=1) / math.log(2.0)).astype(np.float32)
+    od, ld = oracle.decode_ext(q[:, -1:], v, P2[:, -1:], kt, rc, sink_bias=sb, gate_cache=G2,
+                               gate_curr=G2[:, -1:], window_size=window, return_lse=True)
+    np.testing.assert_allclose(od[:, 0], o_full[:, -1], rtol=0, atol=2e-6)
+    np.testing.assert_allclose(ld[:, 0], l_full[:, -1], rtol=4e-7, atol=2e-6)
+
+
+def test_decode_ext_lengths_equal_truncated_forward():
+    """Row b holding len_b tokens of a longer cache decodes as the forward over
+    its first len_b tokens (query at len_b - 1); len_b = 0 gives o = 0 and
+    lse = the sink logit."""
+    B, T, HQ, H, K, V = 3, 140, 4, 2, 16, 8
+    q, k, v, g = _inputs(B, T, HQ, H, K, V, seed=230, g_scale=0.1)
+    sb = _rand((HQ,), 231)
+    P2, kt, rc = _cache_for(k, g)
+    lens = [0, 65, 140]
+    qs = torch.stack([q[b, max(L - 1, 0)] for b, L in enumerate(lens)])[:, None]
+    ps = np.stack([P2[b, max(L - 1, 0)] for b, L in enumerate(lens)])[:, None]
+    od, ld = oracle.decode_ext(qs, v, ps, kt, rc, sink_bias=sb,
+                               cache_seqlens=np.array(lens, dtype=np.int32), return_lse=True)
+    np.testing.assert_array_equal(od[0], 0.0)
+    np.testing.assert_array_equal(ld[0, 0], sb.numpy().astype(np.float64))
+    for b in (1, 2):
+        L = lens[b]
+        of, lf = oracle.wall_attn(q[b:b + 1, :L], k[b:b + 1, :L], v[b:b + 1, :L], g[b:b + 1, :L],
+                                  sink_bias=sb, return_lse=True)
+        np.testing.assert_allclose(od[b, 0], of[0, -1], rtol=0, atol=2e-6)
+        # the float32 cache rounds each score at ~2^-24 relative
+        np.testing.assert_allclose(ld[b, 0], lf[0, -1], rtol=4e-7, atol=2e-6)
