@@ -374,12 +374,62 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
 // in double so that each stored float is the running sum rounded once:
 // decode scores reach ~1e5 on long random-walk decays, where the float error
 // of a float-accumulated scan would show in the lse.
+// Phase A in double: the per-chunk sums of g (per channel) and of g_scalar.
+// grid (cg.size(), nseg), 256 threads; a thread owns CPT channels.
+template <typename TE, int KD>
+__global__ __launch_bounds__(256) void k_chunk_sums_f64(const TE *__restrict__ g,
+                                                        const TE *__restrict__ gs,
+                                                        double *__restrict__ csum,
+                                                        double *__restrict__ csum_s,
+                                                        const int32_t *__restrict__ cu, int64_t T,
+                                                        int HQ, int NCmax, ChunkGrid cg) {
+  int hq, c;
+  if (!cg.map(blockIdx.x, hq, c)) return;
+  const int s = blockIdx.y;
+  int64_t bos, eos;
+  segment_bounds(s, T, cu, bos, eos);
+  const int64_t r0 = bos + (int64_t)c * CHUNK;
+  if (r0 >= eos) return;
+  const int nrow = (eos - r0) < CHUNK ? (int)(eos - r0) : CHUNK;
+  constexpr int CPT = cpt<TE>(), NQ = KD / CPT, NG = 256 / NQ;
+  const int cgi = threadIdx.x % NQ, grp = threadIdx.x / NQ;
+  FV<CPT> xs[CHUNK / NG];
+#pragma unroll
+  for (int i = 0; i < CHUNK / NG; ++i) {
+    const int r = grp + i * NG;
+    xs[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
+  }
+  double acc[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) acc[j] = 0.0;
+#pragma unroll
+  for (int i = 0; i < CHUNK / NG; ++i)
+#pragma unroll
+    for (int j = 0; j < CPT; ++j) acc[j] += (double)xs[i].v[j];
+  __shared__ double red[NG][KD];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) red[grp][CPT * cgi + j] = acc[j];
+  __syncthreads();
+  const int64_t cidx = (int64_t)s * NCmax + c;
+  for (int ch = threadIdx.x; ch < KD; ch += 256) {
+    double t = 0.0;
+    for (int q = 0; q < NG; ++q) t += red[q][ch];
+    csum[(cidx * HQ + hq) * KD + ch] = t;
+  }
+  if (gs != nullptr && threadIdx.x < 64) {
+    double a = (int)threadIdx.x < nrow ? (double)Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
+    if (threadIdx.x == 0) csum_s[cidx * HQ + hq] = a;
+  }
+}
+
 // Phase B in double: exclusive offsets of the chunk sums (channel KD stands
 // for g_scalar).  grid (HQ, nseg, ceil((KD+1)/32)), 256 threads = 32
 // channels x 8 chunk groups.
 template <int KD>
-__global__ __launch_bounds__(256) void k_scan_offsets_f64(const float *__restrict__ csum,
-                                                          const float *__restrict__ csum_s,
+__global__ __launch_bounds__(256) void k_scan_offsets_f64(const double *__restrict__ csum,
+                                                          const double *__restrict__ csum_s,
                                                           double *__restrict__ off,
                                                           double *__restrict__ off_s,
                                                           const int32_t *__restrict__ cu,
@@ -395,7 +445,7 @@ __global__ __launch_bounds__(256) void k_scan_offsets_f64(const float *__restric
   const int span = (nch + 7) / 8;
   const int cb = grp * span, ce = min(nch, cb + span);
   const int64_t c0 = (int64_t)s * NCmax;
-  const float *src;
+  const double *src;
   double *dst;
   int64_t stride;
   if (ch < KD) {
@@ -410,11 +460,11 @@ __global__ __launch_bounds__(256) void k_scan_offsets_f64(const float *__restric
   double tot = 0.0;
   if (active)
     for (int c = cb; c < ce; c += 8) {
-      float x[8];
+      double x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? src[(int64_t)(c + u) * stride] : 0.f;
+      for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? src[(int64_t)(c + u) * stride] : 0.0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) tot += (double)x[u];
+      for (int u = 0; u < 8; ++u) tot += x[u];
     }
   __shared__ double part[8][32];
   part[grp][threadIdx.x & 31] = tot;
@@ -423,14 +473,14 @@ __global__ __launch_bounds__(256) void k_scan_offsets_f64(const float *__restric
   double run = 0.0;
   for (int q = 0; q < grp; ++q) run += part[q][threadIdx.x & 31];
   for (int c = cb; c < ce; c += 8) {
-    float x[8];
+    double x[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? src[(int64_t)(c + u) * stride] : 0.f;
+    for (int u = 0; u < 8; ++u) x[u] = c + u < ce ? src[(int64_t)(c + u) * stride] : 0.0;
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       if (c + u < ce) {
         dst[(int64_t)(c + u) * stride] = run;
-        run += (double)x[u];
+        run += x[u];
       }
   }
 }
@@ -635,15 +685,15 @@ hipError_t prefix_log2_t(const void *g, const void *gs, float *P2, float *G2, co
                          hipStream_t st) {
   const int NCmax = (int)((maxlen + CHUNK - 1) / CHUNK);
   const int64_t n = nseg * NCmax;
-  // workspace: float chunk sums [n, HQ, K] and [n, HQ], then double offsets
-  float *csum = static_cast<float *>(ws);
-  float *csum_s = csum + n * HQ * KD;
-  double *off = reinterpret_cast<double *>(static_cast<char *>(ws) + ((sizeof(float) * n * HQ * (KD + 1) + 255) & ~size_t(255)));
+  // workspace: double chunk sums [n, HQ, K] and [n, HQ], then double offsets
+  double *csum = static_cast<double *>(ws);
+  double *csum_s = csum + n * HQ * KD;
+  double *off = reinterpret_cast<double *>(static_cast<char *>(ws) + ((sizeof(double) * n * HQ * (KD + 1) + 255) & ~size_t(255)));
   double *off_s = off + n * HQ * KD;
   const ChunkGrid cgA = chunk_grid(HQ, 1, NCmax, nseg);
   const dim3 gridA(cgA.size(), (unsigned)nseg);
   const TE *gsp = static_cast<const TE *>(gs);
-  hipLaunchKernelGGL((k_chunk_sums<TE, KD>), gridA, dim3(256), 0, st,
+  hipLaunchKernelGGL((k_chunk_sums_f64<TE, KD>), gridA, dim3(256), 0, st,
                      static_cast<const TE *>(g), gsp, csum, csum_s, cu, T, (int)HQ, NCmax, cgA);
   const dim3 gridB((unsigned)HQ, (unsigned)nseg, (KD + 1 + 31) / 32);
   hipLaunchKernelGGL((k_scan_offsets_f64<KD>), gridB, dim3(256), 0, st, csum, csum_s, off, off_s,
@@ -710,7 +760,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
 
 size_t prefix_workspace_layout(int64_t nseg, int64_t maxlen, int64_t HQ, int64_t K) {
   const int64_t n = nseg * ((maxlen + CHUNK - 1) / CHUNK);
-  return align256(sizeof(float) * n * HQ * (K + 1)) + align256(sizeof(double) * n * HQ * (K + 1));
+  return 2 * align256(sizeof(double) * n * HQ * (K + 1));
 }
 
 hipError_t launch_prefix_phases(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st) {
