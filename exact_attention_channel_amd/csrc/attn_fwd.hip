@@ -146,7 +146,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ, int H, int nseg, int NCmax,
-    int NQT, int window, float qscale) {
+    int NQT, int window, float qscale, const int *__restrict__ wide) {
   // Score product per 32-key tile and wave: S^T = K_tilde Q'^T over DK + 16
   // channels.  The key rows come from the pre-pass with their extra block
   // [1, 1, -Gs_j hi, -Gs_j lo, 0 ...]; the wave's query operand Q' holds
@@ -185,6 +185,9 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   // sequence, sharing most of their key and value tiles in L2.
   const int seg = window > 0 ? rest / NQT : rest % nseg;
   const int I = NQT - 1 - (window > 0 ? rest % NQT : rest / nseg);
+  // a (segment, head) whose decay leaves the half operands' range is done by
+  // the exact kernel instead
+  if (__builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0) return;
   int64_t bos64, eos64;
   segment_bounds(seg, T, cu, bos64, eos64);
   // sequence length (positions below are relative to bos), clamped to the
@@ -246,8 +249,12 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   // All of a wave's loads (g over the chunk up to its last row, q over its
   // rows) go out together, one memory round trip, right after the first tile
   // loads are issued.
+  // exponent bound of this wave's q_hat (max |q_hat| < 2^qexp), folded into
+  // the chunk factors' rebalancing so that Q' = q_hat * d_IJ stays below 2^12
+  int qexp = 0;
   auto make_qhat = [&]() {
     if (!wave_live) return;
+    float qmx = 0.f;
     const int cw = qw0 / CHUNK, r0 = cw * CHUNK;  // the rows' chunk and its first row
     const bool second = qw0 > r0;                 // the wave's rows are the chunk's second half
     float acc[CPL];
@@ -283,13 +290,20 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       }
       float qo[CPL];
 #pragma unroll
-      for (int c = 0; c < CPL; ++c) qo[c] = qv[c] * fast_exp2(acc[c] * LOG2E - rq[c]) * qscale;
+      for (int c = 0; c < CPL; ++c) {
+        qo[c] = qv[c] * fast_exp2(acc[c] * LOG2E - rq[c]) * qscale;
+        qmx = fmaxf(qmx, fabsf(qo[c]));
+      }
       unsigned char *dst = &Qs[(wv * 32 + u) * QSB + 2 * CPL * lane];
       if (CPL == 2)
         *reinterpret_cast<uint32_t *>(dst) = pack_f16x2(qo[0], qo[CPL - 1]);
       else
         *reinterpret_cast<uint16_t *>(dst) = __builtin_bit_cast(uint16_t, (_Float16)qo[0]);
     }
+    qmx = wave_max(qmx);
+    int ex = 0;
+    (void)frexpf(qmx, &ex);  // qmx < 2^ex
+    qexp = __builtin_amdgcn_readfirstlane(max(ex, -8));
   };
   auto load_a = [&](int chunk) {  // anchors of a key chunk, this lane's channels
     const int soff = chunk * HQ * DK * 4;
@@ -326,10 +340,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   auto factors = [&]() -> float {
     float e[CPL];
     bool big = false;
+    // largest factor exponent kept without rebalancing: the half factor
+    // itself below 2^15 and q_hat * factor below 2^12
+    const int cap = min(15, 12 - qexp);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       e[c] = rq[c] - araw[c];
-      big = big || e[c] > 8.f;
+      big = big || e[c] > (float)cap;
     }
     int sigma = 0;
     float csg = 1.f;
@@ -339,7 +356,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       if (CPL == 2) em = fmaxf(em, e[CPL - 1]);
 #pragma unroll
       for (int d = 32; d >= 1; d >>= 1) em = fmaxf(em, __shfl_xor(em, d));
-      sigma = (int)em - 8;
+      sigma = (int)em - cap;
       csg = __builtin_amdgcn_ldexpf(1.f, sigma);
       inv_pend = __builtin_amdgcn_ldexpf(1.f, -sigma);
     }
@@ -814,7 +831,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_f32(
     const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, float *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int nseg, int NCmax, int NCH,
-    int64_t window) {
+    int64_t window, const int *__restrict__ wide) {
   constexpr int QPT = DK / 4, VPT = DV / 4;
   __shared__ float Ks[BN * DK];
   __shared__ float Vs[BN * DV];
@@ -826,6 +843,7 @@ __global__ __launch_bounds__(256) void k_attn_fwd_f32(
   const int rest = blockIdx.x / HQ;
   const int seg = rest % nseg;
   const int c = NCH - 1 - rest / nseg;
+  if (__builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0) return;  // the exact kernel's
   int64_t bos, eos;
   segment_bounds(seg, T, cu, bos, eos);
   const int64_t L = eos - bos;
@@ -927,7 +945,8 @@ hipError_t attn_bf16_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t 
                        static_cast<const _Float16 *>(ws.kt), static_cast<const bf16_t *>(p.v),
                        ws.anch, ws.gsum, p.sink, static_cast<bf16_t *>(p.o), p.lse, p.cu, p.T,
                        p.ntok, (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT,
-                       (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0), p.scale * LOG2E);
+                       (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0), p.scale * LOG2E,
+                       ws.wide);
   };
   if (p.g_scalar != nullptr)
     args(k_attn_fwd_bf16<DK, DV, true>);
@@ -944,7 +963,7 @@ hipError_t attn_f32_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t s
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const float *>(ws.qh),
                        static_cast<const float *>(ws.kt), static_cast<const float *>(p.v),
                        ws.anch, ws.gsum, p.sink, static_cast<float *>(p.o), p.lse, p.cu, p.T,
-                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NCmax, p.window);
+                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NCmax, p.window, ws.wide);
   };
   if (p.g_scalar != nullptr)
     args(k_attn_fwd_f32<DK, DV, true>);

@@ -34,6 +34,7 @@ struct FwdWorkspace {
   void *kt;        // rescaled keys: bf16 path [HQ, ntok, K+16] half with extra
                    // channels, fp32 path [ntok, HQ, K] float
   float *gsum;     // [ntok, HQ] running gate sum (log2 units)
+  int *wide;       // [nseg, HQ] 1: the (segment, head) leaves the anchored operands' range
 };
 
 size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base);
@@ -44,6 +45,7 @@ hipError_t launch_prefix_log2(const void *g, const void *gs, float *P2, float *G
                               const int32_t *cu, int64_t T, int64_t HQ, int64_t K, int64_t nseg,
                               int64_t maxlen, int dtype, void *ws, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st);
+hipError_t launch_attn_exact(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st);
 hipError_t launch_build_cache(const void *k, const float *P2, void *kt, float *rc, int64_t B,
                               int64_t T, int64_t HQ, int64_t H, int64_t K, int dtype,
                               int cache_dtype, hipStream_t st);

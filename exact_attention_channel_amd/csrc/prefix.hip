@@ -126,10 +126,13 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
                                                     float *__restrict__ csum,
                                                     float *__restrict__ csum_s,
                                                     const int32_t *__restrict__ cu, int64_t T,
-                                                    int HQ, int NCmax, ChunkGrid cg) {
+                                                    int HQ, int NCmax, ChunkGrid cg,
+                                                    int *__restrict__ wide) {
   int hq, c;
   if (!cg.map(blockIdx.x, hq, c)) return;
   const int s = blockIdx.y;
+  // the range flags of this call start clear (phase C sets them)
+  if (wide != nullptr && c == 0 && threadIdx.x == 0) wide[s * HQ + hq] = 0;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
   const int64_t r0 = bos + (int64_t)c * CHUNK;
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
     const TE *__restrict__ gs, const float *__restrict__ off, const float *__restrict__ anch,
     const float *__restrict__ off_s, TO *__restrict__ qh, TO *__restrict__ kt,
     float *__restrict__ gsum, const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ,
-    int H, int NCmax, float qscale, ChunkGrid cg) {
+    int H, int NCmax, float qscale, ChunkGrid cg, int *__restrict__ wide) {
   constexpr bool HM = std::is_same<TO, _Float16>::value;  // head-major rows with extras
   constexpr int KX = HM ? KD + 16 : KD;
   int hq, c;
@@ -330,14 +333,26 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   const FV<CPT> A = loadv<float, CPT>(anch + (cidx * HQ + hq) * KD + CPT * cgi);
   FV<CPT> p2[CS::RPG];
   CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
+  // anchor of the query tile (its first chunk): q_hat = q 2^(P2 - RQ)
+  const int64_t cq = (int64_t)s * NCmax + (c & ~1);
+  const FV<CPT> RQ = loadv<float, CPT>(anch + (cq * HQ + hq) * KD + CPT * cgi);
+  // Range of the anchored operands: the exponents of q_hat and k_tilde stay
+  // within EMAX (and the half keys and gate sums below their limits), else
+  // the (segment, head) goes to the exact kernel.  The benchmark workloads
+  // stay below 5.6; a decay sum changing by more than ~8 log2 units inside
+  // one 64-token chunk does not.
+  constexpr float EMAX = HM ? 8.f : 60.f;
+  bool out_of_range = false;
 #pragma unroll
   for (int i = 0; i < CS::RPG; ++i) {
     const int r = grp * CS::RPG + i;
     if (r < nrow) {
       const int64_t t = r0 + r;
+#pragma unroll
+      for (int j = 0; j < CPT; ++j)
+        out_of_range = out_of_range || !(fabsf(A.v[j] - p2[i].v[j]) <= EMAX) ||
+                       !(fabsf(p2[i].v[j] - RQ.v[j]) <= EMAX);
       if (!HM) {  // half operands: the attention kernel forms q_hat itself
-        const int64_t cq = (int64_t)s * NCmax + (c & ~1);
-        const FV<CPT> RQ = loadv<float, CPT>(anch + (cq * HQ + hq) * KD + CPT * cgi);
         const FV<CPT> qv = loadv<TE, CPT>(q + (t * HQ + hq) * KD + CPT * cgi);
         FV<CPT> qo;
 #pragma unroll
@@ -347,10 +362,14 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
       const FV<CPT> kv = loadv<TE, CPT>(k + (t * H + h) * KD + CPT * cgi);
       FV<CPT> ko;
 #pragma unroll
-      for (int j = 0; j < CPT; ++j) ko.v[j] = kv.v[j] * fast_exp2(A.v[j] - p2[i].v[j]);
+      for (int j = 0; j < CPT; ++j) {
+        ko.v[j] = kv.v[j] * fast_exp2(A.v[j] - p2[i].v[j]);
+        if (HM) out_of_range = out_of_range || !(fabsf(ko.v[j]) < 32768.f);
+      }
       storev<TO, CPT>(kt + (HM ? (hq * ntok + t) : (t * HQ + hq)) * KX + CPT * cgi, ko);
     }
   }
+  if (out_of_range) wide[s * HQ + hq] = 1;
   if (threadIdx.x < 64) {
     const int r = threadIdx.x;
     float G = 0.f;
@@ -359,6 +378,8 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
       x = wave_inclusive_scan(x);
       G = (off_s[cidx * HQ + hq] + x) * LOG2E;
       if (r < nrow) gsum[(r0 + r) * HQ + hq] = G;
+      // the half keys carry -G split into two halves
+      if (HM && r < nrow && !(fabsf(G) < 16384.f)) wide[s * HQ + hq] = 1;
     }
     if (HM && r < nrow) {
       const _Float16 gh = (_Float16)(-G);
@@ -666,7 +687,7 @@ hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStrea
   const TE *gs = static_cast<const TE *>(p.g_scalar);
   hipLaunchKernelGGL((k_chunk_sums<TE, KD>), gridA, dim3(256), 0, st,
                      static_cast<const TE *>(p.g), gs, ws.csum, ws.csum_s, p.cu, p.T, (int)p.HQ,
-                     NCmax, cgA);
+                     NCmax, cgA, ws.wide);
   const dim3 gridB((unsigned)p.HQ, (unsigned)p.nseg, (KD + 1 + 31) / 32);
   hipLaunchKernelGGL((k_chunk_scan<KD>), gridB, dim3(256), 0, st, ws.csum, ws.anch, ws.csum_s,
                      p.cu, p.T, (int)p.HQ, NCmax, gs != nullptr ? 1 : 0);
@@ -675,7 +696,7 @@ hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStrea
                      static_cast<const TE *>(p.q), static_cast<const TE *>(p.k),
                      static_cast<const TE *>(p.g), gs, ws.csum, ws.anch, ws.csum_s,
                      static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt), ws.gsum, p.cu, p.T,
-                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC);
+                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC, ws.wide);
   return hipGetLastError();
 }
 
@@ -747,6 +768,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
   char *qh = take(p.dtype == 0 ? 0 : esz * p.ntok * p.HQ * p.K);  // bf16: q_hat formed in the attention kernel
   char *kt = take(esz * p.ntok * p.HQ * (p.dtype == 0 ? p.K + 16 : p.K));
   char *gsum = take(sizeof(float) * p.ntok * p.HQ);
+  char *wide = take(sizeof(int) * p.nseg * p.HQ);
   if (ws) {
     ws->csum = reinterpret_cast<float *>(csum);
     ws->anch = reinterpret_cast<float *>(anch);
@@ -754,6 +776,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
     ws->qh = qh;
     ws->kt = kt;
     ws->gsum = reinterpret_cast<float *>(gsum);
+    ws->wide = reinterpret_cast<int *>(wide);
   }
   return off;
 }

@@ -40,6 +40,11 @@ class Prefill:
     # ln 2, as g is in nats) and channel 0 of k to zero, so the decay sum of
     # that channel climbs steadily without adding to any score
     rise_ch0_log2: float = 0.0
+    # > 0: channels 0 .. fast_ch-1 of g are set to fast_g (natural-log decay
+    # per token) in query heads 0 .. fast_heads-1 (every head if 0)
+    fast_ch: int = 0
+    fast_g: float = 0.0
+    fast_heads: int = 0
 
 
 @dataclasses.dataclass(frozen=True)
@@ -128,6 +133,9 @@ def make_prefill(cfg: Prefill, device="cpu", seed: Optional[int] = None) -> dict
     if cfg.rise_ch0_log2 > 0:
         g[..., 0] = cfg.rise_ch0_log2 * 0.6931471805599453
         k[..., 0] = 0.0
+    if cfg.fast_ch > 0:
+        nh = cfg.fast_heads if cfg.fast_heads > 0 else cfg.HQ
+        g[:, :, :nh, :cfg.fast_ch] = cfg.fast_g
     dt = cfg.dtype
     out = dict(q=q.to(dt), k=k.to(dt), v=v.to(dt), g=g.to(dt),
                g_scalar=None if gs is None else gs.to(dt), sink_bias=sink,

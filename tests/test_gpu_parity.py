@@ -207,6 +207,40 @@ def test_prefill_gate_favouring_old_keys(wa, c):
     check(lse, rl, lse_tol(c.dtype, rl), c.name + " lse")
 
 
+WIDE = [
+    # decay sums that leave the anchored operands' range: the pre-pass sends
+    # these (sequence, head) pairs to the exact kernel
+    cfg("bf16_T1024_strong_decay_gate_sink", 1, 1024, 4, 2, 128, 128, torch.bfloat16,
+        g_mode="neg_softplus", g_std=0.5, g_scalar_std=0.01, sink=True, seed=61),
+    cfg("bf16_T1024_strong_decay_window300", 1, 1024, 4, 2, 128, 128, torch.bfloat16,
+        g_mode="neg_softplus", g_std=0.5, window=300, seed=62),
+    cfg("bf16_T1024_fast_channels", 1, 1024, 4, 2, 128, 128, torch.bfloat16, fast_ch=4,
+        fast_g=-2.0, sink=True, seed=63),
+    # only query head 0 decays fast: heads 1..3 stay on the factorised kernel
+    cfg("bf16_T700_K64_fast_channels_head0", 2, 700, 4, 2, 64, 64, torch.bfloat16, fast_ch=3,
+        fast_g=-2.0, fast_heads=1, g_scalar_std=0.01, seed=64),
+    cfg("bf16_varlen_fast_channels_window90", 1, 0, 4, 1, 128, 64, torch.bfloat16, nseq=5,
+        len_lo=1, len_hi=400, fast_ch=8, fast_g=-2.0, window=90, sink=True, seed=65),
+    cfg("f32_T1024_fast_channels_gate", 1, 1024, 2, 1, 64, 128, torch.float32, fast_ch=4,
+        fast_g=-2.0, g_scalar_std=0.01, sink=True, seed=66),
+    # fp32 operands hold -0.5 softplus decays (no exact kernel)
+    cfg("f32_T600_strong_decay", 1, 600, 2, 1, 128, 64, torch.float32, g_mode="neg_softplus",
+        g_std=0.5, seed=67),
+]
+
+
+@pytest.mark.parametrize("c", WIDE, ids=[c.name for c in WIDE])
+def test_prefill_out_of_operand_range(wa, c):
+    """Strong decays (Wall Attention README, "Features": anchors keep every
+    exp2 bounded only while a chunk's decay span is representable) give the
+    oracle's result, never NaN."""
+    x = W.make_prefill(c)
+    o, lse = run_gpu(wa, x)
+    ro, rl = run_oracle(x)
+    check(o, ro, TOL[c.dtype], c.name + " o")
+    check(lse, rl, lse_tol(c.dtype, rl), c.name + " lse")
+
+
 def boundary_rows(bos, eos, step=64, extra=()):
     rows = set()
     for t in range(bos, eos, step):

@@ -36,6 +36,48 @@ def test_rising_channel_inputs_reach_rebalancing():
     assert float(x["k"][..., 0].abs().max()) == 0.0
 
 
+def operand_exponents(x, chunk=64):
+    """Largest |R_c - P2_j| (the rescaled keys' exponent) and |P2_i - RQ| (the
+    rescaled queries', RQ the anchor of the first chunk of the 128-row query
+    tile) over every (segment, head, channel), in log2 units; anchors are the
+    integer nearest to P2 at each chunk's last token."""
+    g = x["g"].float().numpy().astype(np.float64)
+    cu = x["cu_seqlens"]
+    segs = ([(b, 0, g.shape[1]) for b in range(g.shape[0])] if cu is None
+            else [(0, a, b) for a, b in zip(cu[:-1].tolist(), cu[1:].tolist())])
+    ek = eq = 0.0
+    for b, lo, hi in segs:
+        if hi <= lo:
+            continue
+        P = np.cumsum(g[b, lo:hi], axis=0) / math.log(2)
+        L = P.shape[0]
+        A = np.stack([np.rint(P[min(chunk * c + chunk - 1, L - 1)]) for c in range((L + chunk - 1) // chunk)])
+        cidx = np.arange(L) // chunk
+        ek = max(ek, float(np.abs(A[cidx] - P).max()))
+        eq = max(eq, float(np.abs(P - A[cidx & ~1]).max()))
+    return ek, eq
+
+
+def test_benchmark_workloads_stay_in_the_half_operand_range():
+    """The prefill workloads take the factorised path: both exponents within
+    8 log2 units (the bound past which the pre-pass sends a (sequence, head)
+    to the exact kernel)."""
+    for c in (W.PREFILL_T1024_BF16, W.PREFILL_T8192_BF16, W.VARLEN_W2048_BF16):
+        ek, eq = operand_exponents(W.make_prefill(c))
+        assert ek <= 8 and eq <= 8, (c.name, ek, eq)
+
+
+def test_strong_decay_inputs_leave_the_half_operand_range():
+    """The GPU tests of the exact kernel use decays that overflow the half
+    operands: g = -0.5 softplus(N) (about 37 log2 units per chunk) and
+    channels decaying by 2 nats per token (185 per chunk; beyond float32 too)."""
+    s = W.Prefill("s", 1, 1024, 4, 2, 128, 128, torch.bfloat16, g_mode="neg_softplus", g_std=0.5,
+                  seed=61)
+    f = W.Prefill("f", 1, 1024, 4, 2, 128, 128, torch.bfloat16, fast_ch=4, fast_g=-2.0, seed=63)
+    assert min(operand_exponents(W.make_prefill(s))) > 30
+    assert min(operand_exponents(W.make_prefill(f))) > 130
+
+
 def test_default_workloads_stay_below_rebalancing():
     """The benchmark workload never rebalances (its decay sums fall), so its
     timing is the common path's."""
