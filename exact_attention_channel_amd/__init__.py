@@ -41,7 +41,7 @@ EXPORTED_SYMBOLS = (
     "wall_attn_fwd_prepare", "wall_attn_fwd_attend",
     "wall_attn_prefix_log2_workspace_bytes", "wall_attn_prefix_log2",
     "wall_attn_build_kv_cache", "wall_attn_decode_workspace_bytes", "wall_attn_decode",
-    "wall_attn_decode_ext", "wall_attn_cache_append",
+    "wall_attn_decode_ext", "wall_attn_cache_append", "wall_attn_decode_noalloc",
 )
 
 
@@ -82,6 +82,9 @@ def load_library():
     lib.wall_attn_decode_ext.restype = S
     lib.wall_attn_decode_ext.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, S,
                                          S, P, I, P, I, I, I, P, Z, P]
+    lib.wall_attn_decode_noalloc.restype = S
+    lib.wall_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F,
+                                             S, S, P, I, P, I, I, I, P]
     lib.wall_attn_cache_append.restype = S
     lib.wall_attn_cache_append.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, S, S,
                                            P, I, I, I, P]

@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/wallattn.h"
 #include "common.h"
 #include "launch.h"
@@ -327,6 +329,70 @@ int wall_attn_decode_ext(const void *q, const void *v, const float *p_curr, cons
                      gate_curr, o, lse, B, T_kv, HQ, H, K, V, chunk_size, scale, dtype, cache_dtype,
                      cache_seqlens, window_size, block_table, max_blocks, page_size, num_pages,
                      workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Split partials of wall_attn_decode_noalloc: one array per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in;
+// kernels get the device address from hipGetSymbolAddress, taken once per
+// device with that device current.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WA_HIP_ERROR, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(WA_UNSUPPORTED, "device %d beyond the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(WA_HIP_ERROR, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wall_attn_decode_noalloc(const void *q, const void *v, const float *p_curr,
+                             const void *k_tilde, const float *r_cache, const float *sink_bias,
+                             const float *gate_cache, const float *gate_curr, void *o, float *lse,
+                             int64_t B, int64_t T_kv, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                             int64_t chunk_size, float scale, int dtype, int cache_dtype,
+                             const int32_t *cache_seqlens, int64_t window_size,
+                             const int32_t *block_table, int64_t max_blocks, int64_t page_size,
+                             int64_t num_pages, struct ihipStream_t *stream) {
+  // size check first (host only): the partials must fit the static array
+  int64_t T = T_kv;
+  int rc = check_pages(block_table, max_blocks, page_size, num_pages, &T);
+  if (rc != WA_OK) return rc;
+  rc = check_cache_shape(B, T, HQ, H, K, V, chunk_size, dtype, cache_dtype);
+  if (rc != WA_OK) return rc;
+  const size_t need = wa::decode_workspace_size(B, (T + wa::CHUNK - 1) / wa::CHUNK, HQ, H, V);
+  if (need > kScratchBytes)
+    return fail(WA_UNSUPPORTED, "wall_attn_decode_noalloc: split partials need %zu bytes, above the "
+                                "%zu-byte static scratch (use wall_attn_decode_ext with a workspace)",
+                need, kScratchBytes);
+  void *ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != WA_OK) return rc;
+  return decode_impl("wall_attn_decode_noalloc", q, v, p_curr, k_tilde, r_cache, sink_bias,
+                     gate_cache, gate_curr, o, lse, B, T_kv, HQ, H, K, V, chunk_size, scale, dtype,
+                     cache_dtype, cache_seqlens, window_size, block_table, max_blocks, page_size,
+                     num_pages, ws, kScratchBytes, stream);
 }
 
 int wall_attn_cache_append(const void *k_new, const void *v_new, const float *p_new,

@@ -252,6 +252,30 @@ int wall_attn_decode_ext(const void *q, const void *v, const float *p_curr, cons
                          size_t workspace_bytes, struct ihipStream_t *stream);
 
 /*
+ * wall_attn_decode_ext without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Arguments as wall_attn_decode_ext.  The split
+ * partials go to a static device array of 32 MiB per GPU (held until the
+ * process ends; its address is taken once per device, with hipGetSymbolAddress,
+ * on the first call with that device current -- the current device must be
+ * the one the stream and tensors belong to).  No call allocates or frees
+ * device memory.  Every call on one GPU shares that GPU's array: calls that
+ * overlap on one GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  The array needs no clearing: every call writes all
+ * the partials it reads.
+ * Errors: as wall_attn_decode_ext; UNSUPPORTED when the partials
+ * (wall_attn_decode_workspace_bytes) exceed 32 MiB.
+ */
+int wall_attn_decode_noalloc(const void *q, const void *v, const float *p_curr,
+                             const void *k_tilde, const float *r_cache, const float *sink_bias,
+                             const float *gate_cache, const float *gate_curr, void *o, float *lse,
+                             int64_t B, int64_t T_kv, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                             int64_t chunk_size, float scale, int dtype, int cache_dtype,
+                             const int32_t *cache_seqlens, int64_t window_size,
+                             const int32_t *block_table, int64_t max_blocks, int64_t page_size,
+                             int64_t num_pages, struct ihipStream_t *stream);
+
+/*
  * Streaming append (README "Decode" and "Tests": the sequential-append
  * serving loop that reproduces the forward token by token).  For every batch
  * row b with len_b = cache_seqlens[b] < capacity, the new token goes to
