@@ -56,6 +56,9 @@ def _load():
         lib.oracle_decode_cache_ext.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
                                                 D, P, P]
         lib.oracle_decode_cache_ext.restype = ctypes.c_int
+        lib.oracle_wall_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, I, I, D,
+                                             P, P, P, P, P, P]
+        lib.oracle_wall_attn_bwd.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -213,3 +216,36 @@ def decode_ext(q, v, p_curr, k_tilde, r_cache, sink_bias=None, scale=None, cache
     o = o.reshape(B, 1, HQ, V)
     lse = lse.reshape(B, 1, HQ)
     return (o, lse) if return_lse else o
+
+
+def wall_attn_bwd(q, k, v, g, dO, scale=None, g_scalar=None, sink_bias=None, window_size=None,
+                  cu_seqlens=None):
+    """Gradients of the forward (README introduction: analytic gradients for q,
+    k, v, g; and g_scalar, sink_bias) for dL/do = dO [B,T,HQ,V].
+
+    Returns a dict of float64 arrays: dq [B,T,HQ,K], dk [B,T,H,K],
+    dv [B,T,H,V], dg [B,T,HQ,K], dg_scalar [B,T,HQ] (if g_scalar is given),
+    dsink [HQ] (if sink_bias is given)."""
+    q, k, v, g, dO = _f32(q), _f32(k), _f32(v), _f32(g), _f32(dO)
+    gs, sink, cu = _f32(g_scalar), _f32(sink_bias), _i32(cu_seqlens)
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
+    if scale is None:
+        scale = K ** -0.5
+    nseq = 0 if cu is None else cu.shape[0] - 1
+    W = 0 if window_size is None else int(window_size)
+    out = dict(dq=np.zeros(q.shape), dk=np.zeros(k.shape), dv=np.zeros(v.shape),
+               dg=np.zeros(g.shape))
+    dgs = np.zeros((B, T, HQ)) if gs is not None else None
+    dsk = np.zeros(HQ) if sink is not None else None
+    r = _load().oracle_wall_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gs), _ptr(sink),
+                                     _ptr(dO), B, T, HQ, H, K, V, _ptr(cu), nseq, W, float(scale),
+                                     _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                     _ptr(out["dg"]), _ptr(dgs), _ptr(dsk))
+    if r != 0:
+        raise ValueError("oracle_wall_attn_bwd: bad arguments")
+    if dgs is not None:
+        out["dg_scalar"] = dgs
+    if dsk is not None:
+        out["dsink"] = dsk
+    return out

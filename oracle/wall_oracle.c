@@ -370,3 +370,131 @@ int oracle_decode_cache_ext(const float *q, const float *v, const float *p_curr,
   }
   return 0;
 }
+
+/*
+ * Gradients of the forward (Wall Attention README, introduction: "fused
+ * forward + backward kernels with analytic gradients for q, k, v, g"; its
+ * tests check the gradients of g and g_scalar against central finite
+ * differences).  For a loss L with dL/do = dO, written from the forward's
+ * definition above:
+ *   p_ij   = exp(s_ij - lse_i)  (j in S_i),   p_sink_i = exp(sink - lse_i)
+ *   dv_j   = sum_i p_ij dO_i                             (summed over the query heads of v's head)
+ *   dp_ij  = dO_i . v_j,   D_i = sum_j p_ij dp_ij,   ds_ij = p_ij (dp_ij - D_i)
+ *   dsink  = -sum_i p_sink_i D_i                         (the sink logit has no value)
+ *   a_ijn  = scale q_in k_jn exp(P_in - P_jn)             (so s_ij = sum_n a_ijn + Gs_i - Gs_j)
+ *   dq_in  = sum_j ds_ij a_ijn / q_in  = scale sum_j ds_ij k_jn exp(P_in - P_jn)
+ *   dk_jn  = scale sum_i ds_ij q_in exp(P_in - P_jn)      (summed over the query heads of k's head)
+ *   dP_tn  = sum_j ds_tj a_tjn - sum_i ds_it a_itn        (P_t enters as the query's and the key's prefix)
+ *   dGs_t  = sum_j ds_tj - sum_i ds_it
+ *   dg_un  = sum_{t >= u, same segment} dP_tn,   dg_scalar_u = sum_{t >= u} dGs_t
+ * Every array is double; inputs as oracle_wall_attn_fwd; dO [Ntok,HQ,V].
+ * dg_scalar and dsink may be NULL.  Returns 0, or -1 on a bad argument.
+ */
+int oracle_wall_attn_bwd(const float *q, const float *k, const float *v, const float *g,
+                         const float *g_scalar, const float *sink, const float *dO,
+                         int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                         const int32_t *cu_seqlens, int64_t nseq, int64_t window, double scale,
+                         double *dq, double *dk, double *dv, double *dg, double *dg_scalar,
+                         double *dsink) {
+  if (H <= 0 || HQ <= 0 || HQ % H != 0 || K <= 0 || V <= 0) return -1;
+  if (cu_seqlens && B != 1) return -1;
+  int64_t nseg = cu_seqlens ? nseq : B;
+  int64_t ntok = cu_seqlens ? (int64_t)cu_seqlens[nseq] : B * T;
+  int64_t group = HQ / H;
+  double *P = (double *)malloc(sizeof(double) * (size_t)(ntok * HQ * K));
+  double *Gs = (double *)malloc(sizeof(double) * (size_t)(ntok * HQ));
+  double *dP = (double *)calloc((size_t)(ntok * HQ * K), sizeof(double));
+  double *dGs = (double *)calloc((size_t)(ntok * HQ), sizeof(double));
+  double *dsk = (double *)calloc((size_t)HQ, sizeof(double));
+  if (!P || !Gs || !dP || !dGs || !dsk) { free(P); free(Gs); free(dP); free(dGs); free(dsk); return -1; }
+  prefix_sums(g, g_scalar, nseg, T, cu_seqlens, HQ, K, P, Gs);
+  memset(dq, 0, sizeof(double) * (size_t)(ntok * HQ * K));
+  memset(dk, 0, sizeof(double) * (size_t)(ntok * H * K));
+  memset(dv, 0, sizeof(double) * (size_t)(ntok * H * V));
+  /* Sequential over (segment, query head, row): the key-side sums (dk, dv,
+   * the key's share of dP and dGs) accumulate from many rows. */
+  for (int64_t s = 0; s < nseg; ++s) {
+    int64_t bos, eos;
+    segment(s, T, cu_seqlens, &bos, &eos);
+    for (int64_t hq = 0; hq < HQ; ++hq) {
+      int64_t h = hq / group;
+      for (int64_t i = bos; i < eos; ++i) {
+        int64_t jlo = bos;
+        if (window > 0 && i - window + 1 > jlo) jlo = i - window + 1;
+        int64_t n_j = i - jlo + 1;
+        double *sc = (double *)malloc(sizeof(double) * (size_t)n_j);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)n_j);
+        const float *qi = q + (i * HQ + hq) * K;
+        const double *Pi = P + (i * HQ + hq) * K;
+        const float *dOi = dO + (i * HQ + hq) * V;
+        /* forward statistics of row i */
+        double m = -INFINITY;
+        for (int64_t j = jlo; j <= i; ++j) {
+          const float *kj = k + (j * H + h) * K;
+          const double *Pj = P + (j * HQ + hq) * K;
+          double dot = 0.0;
+          for (int64_t n = 0; n < K; ++n) dot += (double)qi[n] * (double)kj[n] * exp(Pi[n] - Pj[n]);
+          sc[j - jlo] = scale * dot + (Gs[i * HQ + hq] - Gs[j * HQ + hq]);
+          if (sc[j - jlo] > m) m = sc[j - jlo];
+        }
+        if (sink && (double)sink[hq] > m) m = (double)sink[hq];
+        double Z = 0.0;
+        for (int64_t j = jlo; j <= i; ++j) Z += exp(sc[j - jlo] - m);
+        if (sink) Z += exp((double)sink[hq] - m);
+        double lse = m + log(Z);
+        /* dp, D */
+        double D = 0.0;
+        for (int64_t j = jlo; j <= i; ++j) {
+          const float *vj = v + (j * H + h) * V;
+          double t = 0.0;
+          for (int64_t c = 0; c < V; ++c) t += (double)dOi[c] * (double)vj[c];
+          dp[j - jlo] = t;
+          D += exp(sc[j - jlo] - lse) * t;
+        }
+        if (sink) dsk[hq] -= exp((double)sink[hq] - lse) * D;
+        for (int64_t j = jlo; j <= i; ++j) {
+          const float *kj = k + (j * H + h) * K;
+          const float *vj = v + (j * H + h) * V;
+          const double *Pj = P + (j * HQ + hq) * K;
+          double p = exp(sc[j - jlo] - lse);
+          double ds = p * (dp[j - jlo] - D);
+          for (int64_t c = 0; c < V; ++c) dv[(j * H + h) * V + c] += p * (double)dOi[c];
+          for (int64_t n = 0; n < K; ++n) {
+            double a = scale * (double)qi[n] * (double)kj[n] * exp(Pi[n] - Pj[n]);
+            dq[(i * HQ + hq) * K + n] += ds * scale * (double)kj[n] * exp(Pi[n] - Pj[n]);
+            dk[(j * H + h) * K + n] += ds * scale * (double)qi[n] * exp(Pi[n] - Pj[n]);
+            dP[(i * HQ + hq) * K + n] += ds * a;
+            dP[(j * HQ + hq) * K + n] -= ds * a;
+          }
+          dGs[i * HQ + hq] += ds;
+          dGs[j * HQ + hq] -= ds;
+        }
+        free(sc);
+        free(dp);
+      }
+      /* reverse running sums within the segment */
+      for (int64_t n = 0; n < K; ++n) {
+        double acc = 0.0;
+        for (int64_t t = eos - 1; t >= bos; --t) {
+          acc += dP[(t * HQ + hq) * K + n];
+          dg[(t * HQ + hq) * K + n] = acc;
+        }
+      }
+      if (dg_scalar) {
+        double acc = 0.0;
+        for (int64_t t = eos - 1; t >= bos; --t) {
+          acc += dGs[t * HQ + hq];
+          dg_scalar[t * HQ + hq] = acc;
+        }
+      }
+    }
+  }
+  if (dsink)
+    for (int64_t hq = 0; hq < HQ; ++hq) dsink[hq] = sink ? dsk[hq] : 0.0;
+  free(P);
+  free(Gs);
+  free(dP);
+  free(dGs);
+  free(dsk);
+  return 0;
+}
