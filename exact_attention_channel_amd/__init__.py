@@ -25,7 +25,7 @@ import os
 
 import torch
 
-__all__ = ["wall_attn", "wall_attn_prefix_log2", "build_wall_kv_cache", "wall_attn_decode",
+__all__ = ["wall_attn", "wall_attn_bwd", "wall_attn_prefix_log2", "build_wall_kv_cache", "wall_attn_decode",
            "wall_attn_cache_append", "cache_dtype", "library_path", "load_library",
            "EXPORTED_SYMBOLS"]
 
@@ -42,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "wall_attn_prefix_log2_workspace_bytes", "wall_attn_prefix_log2",
     "wall_attn_build_kv_cache", "wall_attn_decode_workspace_bytes", "wall_attn_decode",
     "wall_attn_decode_ext", "wall_attn_cache_append", "wall_attn_decode_noalloc",
+    "wall_attn_bwd_workspace_bytes", "wall_attn_bwd",
 )
 
 
@@ -85,6 +86,10 @@ def load_library():
     lib.wall_attn_decode_noalloc.restype = S
     lib.wall_attn_decode_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, F,
                                              S, S, P, I, P, I, I, I, P]
+    lib.wall_attn_bwd_workspace_bytes.restype = Z
+    lib.wall_attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I, I, I, S]
+    lib.wall_attn_bwd.restype = S
+    lib.wall_attn_bwd.argtypes = [P] * 15 + [I] * 6 + [P, I, I, I, F, S, P, Z, P]
     lib.wall_attn_cache_append.restype = S
     lib.wall_attn_cache_append.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, S, S,
                                            P, I, I, I, P]
@@ -202,6 +207,43 @@ def wall_attn(q, k, v, g, scale=None, g_scalar=None, sink_bias=None, window_size
                            _stream(dev))
     _check(rc, "wall_attn")
     return (o, lse) if return_lse else o
+
+
+def wall_attn_bwd(q, k, v, g, o, lse, dO, scale=None, g_scalar=None, sink_bias=None,
+                  window_size=None, cu_seqlens=None, max_seqlen=None, check_max_seqlen=True):
+    """Gradients of wall_attn for dL/do = dO (README introduction: analytic
+    gradients for q, k, v, g and the gate), from the forward's output o and
+    its lse (``wall_attn(..., return_lse=True)``).
+
+    Returns (dq, dk, dv, dg, dg_scalar, dsink): dg_scalar is None without
+    g_scalar, dsink (float32 [HQ]) None without sink_bias."""
+    lib = load_library()
+    dev = _dev(q, k, v, g, o, lse, dO, g_scalar, sink_bias, cu_seqlens)
+    code = _dtype_code(q)
+    _same_dtype(q, k, v, g, o, dO, g_scalar)
+    _f32(sink_bias, lse)
+    B, T, HQ, K = q.shape
+    H, V = k.shape[2], v.shape[3]
+    if (tuple(k.shape) != (B, T, H, K) or tuple(v.shape) != (B, T, H, V)
+            or tuple(g.shape) != (B, T, HQ, K) or tuple(o.shape) != (B, T, HQ, V)
+            or tuple(dO.shape) != (B, T, HQ, V) or tuple(lse.shape) != (B, T, HQ)):
+        raise ValueError("shapes must be q [B,T,HQ,K], k [B,T,H,K], v [B,T,H,V], g [B,T,HQ,K], "
+                         "o and dO [B,T,HQ,V], lse [B,T,HQ]")
+    nseq, max_seqlen = _varlen(cu_seqlens, max_seqlen, check_max_seqlen)
+    dq, dg = torch.empty_like(q), torch.empty_like(g)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    dgs = None if g_scalar is None else torch.empty_like(g_scalar)
+    dsink = None if sink_bias is None else torch.empty_like(sink_bias)
+    need = lib.wall_attn_bwd_workspace_bytes(B, T, HQ, H, K, V, nseq, max_seqlen, code)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    W = 0 if window_size is None else int(window_size)
+    s = 0.0 if scale is None else float(scale)
+    rc = lib.wall_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(g_scalar), _ptr(sink_bias),
+                           _ptr(o), _ptr(lse), _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                           _ptr(dgs), _ptr(dsink), B, T, HQ, H, K, V, _ptr(cu_seqlens), nseq,
+                           max_seqlen, W, s, code, _ptr(ws), ws.numel(), _stream(dev))
+    _check(rc, "wall_attn_bwd")
+    return dq, dk, dv, dg, dgs, dsink
 
 
 def fwd_workspace_bytes(B, T, HQ, H, K, V, num_seqs=0, max_seqlen=0, dtype=torch.bfloat16):

@@ -161,6 +161,57 @@ int wall_attn_fwd_attend(const void *q, const void *v, const void *g, const void
                   dtype, workspace, workspace_bytes, stream);
 }
 
+size_t wall_attn_bwd_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K,
+                                     int64_t V, int64_t num_seqs, int64_t max_seqlen, int dtype) {
+  wa::FwdProblem p{};
+  const bool varlen = num_seqs > 0;
+  if (check_fwd_shape(B, T, HQ, H, K, V, varlen, num_seqs, max_seqlen, dtype, &p) != WA_OK) return 0;
+  return wa::fwd_workspace_layout(p, nullptr, nullptr) + wa::bwd_workspace_layout(p, nullptr, nullptr);
+}
+
+int wall_attn_bwd(const void *q, const void *k, const void *v, const void *g,
+                  const void *g_scalar, const float *sink_bias, const void *o, const float *lse,
+                  const void *dO, void *dq, void *dk, void *dv, void *dg, void *dg_scalar,
+                  float *dsink, int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                  const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                  int64_t window_size, float scale, int dtype, void *workspace,
+                  size_t workspace_bytes, struct ihipStream_t *stream) {
+  wa::BwdProblem b{};
+  int rc = check_fwd_shape(B, T, HQ, H, K, V, cu_seqlens != nullptr, num_seqs, max_seqlen, dtype, &b.f);
+  if (rc != WA_OK) return rc;
+  if (!q || !k || !v || !g || !o || !lse || !dO || !dq || !dk || !dv || !dg || !workspace)
+    return fail(WA_INVALID_ARG, "wall_attn_bwd: q, k, v, g, o, lse, dO, dq, dk, dv, dg and workspace must be non-NULL");
+  if ((g_scalar == nullptr) != (dg_scalar == nullptr))
+    return fail(WA_INVALID_ARG, "wall_attn_bwd: g_scalar and dg_scalar must be given together");
+  if (dsink != nullptr && sink_bias == nullptr)
+    return fail(WA_INVALID_ARG, "wall_attn_bwd: dsink needs sink_bias");
+  const void *ptrs[] = {q, k, v, g, g_scalar, sink_bias, o, lse, dO, dq, dk, dv, dg, dg_scalar,
+                        dsink, workspace};
+  for (const void *ptr : ptrs)
+    if (ptr && !aligned16(ptr)) return fail(WA_INVALID_ARG, "device pointers must be 16-byte aligned");
+  const size_t nf = wa::fwd_workspace_layout(b.f, nullptr, nullptr);
+  const size_t need = nf + wa::bwd_workspace_layout(b.f, nullptr, nullptr);
+  if (workspace_bytes < need)
+    return fail(WA_WORKSPACE_TOO_SMALL, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+  wa::FwdProblem &p = b.f;
+  p.q = q; p.k = k; p.v = v; p.g = g; p.g_scalar = g_scalar; p.sink = sink_bias;
+  p.o = nullptr; p.lse = nullptr; p.cu = cu_seqlens;
+  p.window = window_size > 0 ? window_size : 0;
+  p.scale = scale > 0.f ? scale : 1.0f / sqrtf((float)K);
+  b.o = o; b.dO = dO; b.lse = lse; b.dq = dq; b.dk = dk; b.dv = dv; b.dg = dg; b.dgs = dg_scalar;
+  b.dsink = dsink;
+  wa::FwdWorkspace ws{};
+  wa::fwd_workspace_layout(p, &ws, static_cast<char *>(workspace));
+  wa::BwdWorkspace bw{};
+  wa::bwd_workspace_layout(p, &bw, static_cast<char *>(workspace) + nf);
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  // the running sums (chunk offsets, gate sums) come from the forward's pre-pass
+  hipError_t e = wa::launch_prefix_phases(p, ws, st);
+  if (e == hipSuccess) e = wa::launch_attn_bwd(b, ws, bw, st);
+  if (e != hipSuccess) return fail(WA_HIP_ERROR, "wall_attn_bwd launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t wall_attn_prefix_log2_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t K,
                                              int64_t num_seqs, int64_t max_seqlen) {
   const bool varlen = num_seqs > 0;

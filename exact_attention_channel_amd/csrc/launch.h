@@ -50,6 +50,24 @@ hipError_t launch_build_cache(const void *k, const float *P2, void *kt, float *r
                               int64_t T, int64_t HQ, int64_t H, int64_t K, int dtype,
                               int cache_dtype, hipStream_t st);
 
+// Backward pass of the prefill.
+struct BwdProblem {
+  FwdProblem f;                     // inputs and shapes as the forward
+  const void *o, *dO;               // forward output and dL/do (dtype)
+  const float *lse;                 // forward lse
+  void *dq, *dk, *dv, *dg, *dgs;    // gradients (dtype); dgs NULL without g_scalar
+  float *dsink;                     // [HQ] or NULL
+};
+struct BwdWorkspace {
+  float *Dv, *psD;                  // [ntok, HQ] D_i, exp(sink - lse_i) D_i
+  float *dq32, *dk_part, *dv_part;  // [ntok, HQ, K|V]: dq, each query head's dk and dv
+  float *rows_ds, *cols_ds;         // [ntok, HQ] row and column sums of ds
+  float *ctot;                      // [nseg*NCmax, HQ, K+1] chunk totals of dP and dGs
+};
+size_t bwd_workspace_layout(const FwdProblem &p, BwdWorkspace *bw, char *base);
+hipError_t launch_attn_bwd(const BwdProblem &b, const FwdWorkspace &ws, const BwdWorkspace &bw,
+                           hipStream_t st);
+
 // Element types (the values of the public WA_BF16 / WA_F32 / WA_F16).
 enum { WA_DT_BF16 = 0, WA_DT_F32 = 1, WA_DT_F16 = 2 };
 

@@ -144,6 +144,42 @@ int wall_attn_fwd_attend(const void *q, const void *v, const void *g, const void
                          int dtype, void *workspace, size_t workspace_bytes,
                          struct ihipStream_t *stream);
 
+/* Bytes of device workspace wall_attn_bwd needs (0 on bad arguments);
+ * arguments as wall_attn_fwd_workspace_bytes. */
+size_t wall_attn_bwd_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K,
+                                     int64_t V, int64_t num_seqs, int64_t max_seqlen, int dtype);
+
+/*
+ * Backward pass of wall_attn_fwd (README introduction: analytic gradients
+ * for q, k, v, g and the scalar gate; the FlashAttention papers'
+ * recomputation from the stored o and lse).  For a loss with dL/do = dO,
+ * with p_ij = exp(s_ij - lse_i), D_i = dO_i . o_i and
+ * ds_ij = p_ij (dO_i . v_j - D_i):
+ *   dv_j  = sum_i p_ij dO_i                        (summed over v's query heads)
+ *   dq_in = scale sum_j ds_ij k_jn exp(P_in - P_jn)
+ *   dk_jn = scale sum_i ds_ij q_in exp(P_in - P_jn) (summed over k's query heads)
+ *   dg    = reverse running sum, within each sequence, of
+ *           dP_tn = q_tn dq_tn - k_tn dk(hq)_tn   (dk(hq): the head's own share)
+ *   dg_scalar = reverse running sum of sum_j ds_tj - sum_i ds_it
+ *   dsink[hq] = -sum_i exp(sink_bias[hq] - lse_i) D_i.
+ *   Inputs as wall_attn_fwd, plus o [B,T,HQ,V] and lse [B,T,HQ] from the
+ *   forward and dO [B,T,HQ,V] (dtype).  Outputs (caller-owned): dq, dg
+ *   [B,T,HQ,K], dk [B,T,H,K], dv [B,T,H,V] in dtype; dg_scalar [B,T,HQ]
+ *   (given exactly when g_scalar is); dsink [HQ] float32 or NULL (needs
+ *   sink_bias).  Every factor exp(P_in - P_jn) is formed per pair, so any
+ *   decay rate is held; arithmetic in float32.  Rows past max_seqlen (see
+ *   wall_attn_fwd) get unspecified gradients.
+ * Errors: as wall_attn_fwd; INVALID_ARG for a gate or sink gradient without
+ * its input.
+ */
+int wall_attn_bwd(const void *q, const void *k, const void *v, const void *g,
+                  const void *g_scalar, const float *sink_bias, const void *o, const float *lse,
+                  const void *dO, void *dq, void *dk, void *dv, void *dg, void *dg_scalar,
+                  float *dsink, int64_t B, int64_t T, int64_t HQ, int64_t H, int64_t K, int64_t V,
+                  const int32_t *cu_seqlens, int64_t num_seqs, int64_t max_seqlen,
+                  int64_t window_size, float scale, int dtype, void *workspace,
+                  size_t workspace_bytes, struct ihipStream_t *stream);
+
 /* Bytes of device workspace wall_attn_prefix_log2 needs (0 on bad arguments). */
 size_t wall_attn_prefix_log2_workspace_bytes(int64_t B, int64_t T, int64_t HQ, int64_t K,
                                              int64_t num_seqs, int64_t max_seqlen);
