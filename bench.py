@@ -44,6 +44,7 @@ import time
 METRIC = "prefill TFLOP/s (% bf16 MFMA peak) at T=8K; decode GB/s (% HBM peak)"
 PEAK_MFMA_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E, published
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector, published
 
 
 def parse():
@@ -57,6 +58,7 @@ def parse():
     ap.add_argument("--settle", type=float, default=0.5,
                     help="seconds of untimed launches after the warm-up steps, before timing")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-row-stride", type=int, default=1,
                     help="oracle baseline evaluates every n-th query row")
@@ -294,6 +296,46 @@ def main():
                      "traffic": recorded_traffic("attend"), "kernel_ms": round(ms_attn, 4)},
         "prefill_breakdown_ms": {"prepare": round(ms_prep, 4), "attend": round(ms_attn, 4)},
     }
+
+    # ------------------------------------------------------------------ backward
+    if not args.no_backward:
+        xb = W.make_prefill(c, device=dev)
+        ob, lb = wa.wall_attn(xb["q"], xb["k"], xb["v"], xb["g"], scale=xb["scale"],
+                              g_scalar=xb["g_scalar"], sink_bias=xb["sink_bias"], return_lse=True)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        dO = torch.randn(ob.shape, generator=gen, device=dev).to(ob.dtype)
+        grads = [torch.empty_like(xb[n]) for n in ("q", "k", "v", "g", "g_scalar")]
+        dsink = torch.empty_like(xb["sink_bias"])
+        bwb = lib.wall_attn_bwd_workspace_bytes(B, T, HQ, H, K, V, 0, 0, wa.WA_BF16)
+        bws = torch.empty(bwb, dtype=torch.uint8, device=dev)
+
+        def bwd():
+            rc = lib.wall_attn_bwd(ptr(xb["q"]), ptr(xb["k"]), ptr(xb["v"]), ptr(xb["g"]),
+                                   ptr(xb["g_scalar"]), ptr(xb["sink_bias"]), ptr(ob), ptr(lb),
+                                   ptr(dO), *[ptr(t) for t in grads[:4]], ptr(grads[4]),
+                                   ptr(dsink), B, T, HQ, H, K, V, None, 0, 0, 0, scale,
+                                   wa.WA_BF16, ptr(bws), bwb, stream)
+            if rc:
+                raise RuntimeError(lib.wall_attn_last_error().decode())
+
+        bwd()
+        nb = max(2, min(args.steps, 5))
+        ms_bwd = event_time_ms(bwd, nb, torch)
+        # per visible pair and head: scores 2K, dO.v 2V, dv 2V, dq 2K, dk 2K
+        bflops = 2.0 * HQ * (3 * K + 2 * V) * causal_pairs([T] * B)
+        btf = bflops / (ms_bwd * 1e-3) / 1e12
+        log(f"[bench] backward {ms_bwd:.3f} ms, {btf:.1f} TFLOP/s")
+        out["backward"] = {
+            "workload": c.name, "call": "wall_attn_bwd", "ms": round(ms_bwd, 3),
+            "gflop": round(bflops / 1e9, 3), "TFLOP/s": round(btf, 2), "launches_timed": nb,
+            "roofline": {"kernel": "k_bwd_dq + k_bwd_dkdv (float32 FMA, one exp2 per pair and channel)",
+                         "bound": "alu", "achieved": round(btf, 2), "peak": PEAK_FP32_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(btf / PEAK_FP32_TFLOPS, 4),
+                         "traffic": None},
+        }
+        del xb, ob, lb, dO, grads, dsink, bws
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ other workloads
     # the remaining prefill workloads (tiny fp32, usage shape, packed varlen
