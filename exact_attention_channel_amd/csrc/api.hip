@@ -204,6 +204,7 @@ int wall_attn_bwd(const void *q, const void *k, const void *v, const void *g,
   wa::fwd_workspace_layout(p, &ws, static_cast<char *>(workspace));
   wa::BwdWorkspace bw{};
   wa::bwd_workspace_layout(p, &bw, static_cast<char *>(workspace) + nf);
+  ws.qbh = bw.qbh;  // the pre-pass also writes the backward's half query operand
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   // the running sums (chunk offsets, gate sums) come from the forward's pre-pass
   hipError_t e = wa::launch_prefix_phases(p, ws, st);

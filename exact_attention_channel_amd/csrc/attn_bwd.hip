@@ -13,16 +13,22 @@
 //   dGs_t = sum_j ds_tj - sum_i ds_it,
 //   dg = reverse running sum of dP within each sequence, dg_scalar likewise
 //   of dGs, dsink = -sum_i exp(sink - lse_i) D_i.
-// Every (i, j) factor e^(P_in - P_jn) is formed on its own as
-// 2^(P2_in - P2_jn) (one exp2 per channel and pair, the exact kernel's
-// arithmetic), so the backward holds for every decay rate; float32
+// The pair products (dq, dk, dv and the row and column sums of ds) run on
+// the matrix cores for bf16 inputs (attn_bwd_mfma.hip).  The kernels here
+// take float32 inputs and the (sequence, head) pairs the pre-pass flags as
+// outside the anchored operands' range: every (i, j) factor e^(P_in - P_jn)
+// is formed on its own as 2^(P2_in - P2_jn) (one exp2 per channel and pair,
+// the exact kernel's arithmetic), so they hold for every decay rate; float32
 // throughout, plain FMAs.
 //
 // Kernels: D and the sink terms per row; dq (a workgroup per query chunk,
 // walking its key chunks); dk, dv (a workgroup per key chunk, walking the
-// query chunks that see it), each head's share kept apart; then the sums
-// over a key/value head's query heads and the reverse running sums.
+// query chunks that see it), each head's share kept apart; then, for both
+// paths, the sums over a key/value head's query heads and the reverse
+// running sums.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -81,7 +87,7 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
     const TE *__restrict__ g, const TE *__restrict__ dO, const float *__restrict__ off,
     const float *__restrict__ gsum, const float *__restrict__ lse, const float *__restrict__ Dv,
     float *__restrict__ dq32, float *__restrict__ rows_ds, const int32_t *__restrict__ cu,
-    int64_t T, int HQ, int H, int NCmax, int window, float scale) {
+    const int *__restrict__ wide, int64_t T, int HQ, int H, int NCmax, int window, float scale) {
   constexpr int QPT = DK / 4, VPT = DV / 4;
   __shared__ float Ks[XC * DK];
   __shared__ float Pk[XC * DK];
@@ -90,6 +96,8 @@ __global__ __launch_bounds__(256) void k_bwd_dq(
   __shared__ float tot[256];
   const int tid = threadIdx.x;
   const int sh = blockIdx.x, seg = sh / HQ, hq = sh % HQ;
+  // with flags given, only the flagged pairs (the matrix-core kernels take the rest)
+  if (wide != nullptr && __builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) == 0) return;
   int64_t bos, eos;
   segment_bounds(seg, T, cu, bos, eos);
   const int L = (int)min(eos - bos, (int64_t)NCmax * XC);
@@ -179,7 +187,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
     const TE *__restrict__ g, const TE *__restrict__ dO, const float *__restrict__ off,
     const float *__restrict__ gsum, const float *__restrict__ lse, const float *__restrict__ Dv,
     float *__restrict__ dk_part, float *__restrict__ dv_part, float *__restrict__ cols_ds,
-    const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int NCmax, int window, float scale) {
+    const int32_t *__restrict__ cu, const int *__restrict__ wide, int64_t T, int HQ, int H,
+    int NCmax, int window, float scale) {
   constexpr int KPT = DK / 4, VPT = DV / 4;
   __shared__ float Qs[XC * DK];
   __shared__ float Pq[XC * DK];
@@ -188,6 +197,8 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
   __shared__ float tot[256];
   const int tid = threadIdx.x;
   const int sh = blockIdx.x, seg = sh / HQ, hq = sh % HQ;
+  // with flags given, only the flagged pairs (the matrix-core kernels take the rest)
+  if (wide != nullptr && __builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) == 0) return;
   int64_t bos, eos;
   segment_bounds(seg, T, cu, bos, eos);
   const int L = (int)min(eos - bos, (int64_t)NCmax * XC);
@@ -400,14 +411,22 @@ hipError_t bwd_t(const BwdProblem &b, const FwdWorkspace &ws, const BwdWorkspace
   hipLaunchKernelGGL((k_bwd_rows<TE, DV>), dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st,
                      static_cast<const TE *>(b.o), dO, b.lse, p.sink, bw.Dv, bw.psD, nrows,
                      (int)p.HQ);
+  // half-operand inputs: the matrix-core kernels take the pairs within the
+  // anchored operands' range, these float32 kernels the flagged ones
+  const bool mfma = std::is_same<TE, bf16_t>::value;
+  const int *fl = mfma ? ws.wide : nullptr;
+  if (mfma) {
+    const hipError_t e = launch_attn_bwd_mfma(b, ws, bw, st);
+    if (e != hipSuccess) return e;
+  }
   const dim3 grid((unsigned)(p.nseg * p.HQ), (unsigned)(NCmax < 16 ? NCmax : 16));
   auto dq_k = p.g_scalar != nullptr ? k_bwd_dq<TE, DK, DV, true> : k_bwd_dq<TE, DK, DV, false>;
   hipLaunchKernelGGL(dq_k, grid, dim3(256), 0, st, q, k, v, g, dO, ws.csum, ws.gsum, b.lse, bw.Dv,
-                     bw.dq32, bw.rows_ds, p.cu, p.T, (int)p.HQ, (int)p.H, NCmax, W, p.scale);
+                     bw.dq32, bw.rows_ds, p.cu, fl, p.T, (int)p.HQ, (int)p.H, NCmax, W, p.scale);
   auto kv_k = p.g_scalar != nullptr ? k_bwd_dkdv<TE, DK, DV, true> : k_bwd_dkdv<TE, DK, DV, false>;
   hipLaunchKernelGGL(kv_k, grid, dim3(256), 0, st, q, k, v, g, dO, ws.csum, ws.gsum, b.lse, bw.Dv,
-                     bw.dk_part, bw.dv_part, bw.cols_ds, p.cu, p.T, (int)p.HQ, (int)p.H, NCmax, W,
-                     p.scale);
+                     bw.dk_part, bw.dv_part, bw.cols_ds, p.cu, fl, p.T, (int)p.HQ, (int)p.H, NCmax,
+                     W, p.scale);
   const dim3 gridc((unsigned)(NCmax * p.HQ), (unsigned)p.nseg);
   hipLaunchKernelGGL((k_bwd_chunk_totals<TE, DK>), gridc, dim3(256), 0, st, q, k, bw.dq32,
                      bw.dk_part, bw.rows_ds, bw.cols_ds, bw.ctot, p.cu, p.T, (int)p.HQ, (int)p.H,
@@ -456,9 +475,11 @@ size_t bwd_workspace_layout(const FwdProblem &p, BwdWorkspace *bw, char *base) {
   float *rows_ds = take(sizeof(float) * nrows);
   float *cols_ds = take(sizeof(float) * nrows);
   float *ctot = take(sizeof(float) * p.nseg * NCmax * p.HQ * (p.K + 1));
+  float *qbh = take(p.dtype == WA_DT_BF16 ? sizeof(uint16_t) * nrows * p.K : 0);
   if (bw) {
     bw->Dv = Dv; bw->psD = psD; bw->dq32 = dq32; bw->dk_part = dk_part; bw->dv_part = dv_part;
     bw->rows_ds = rows_ds; bw->cols_ds = cols_ds; bw->ctot = ctot;
+    bw->qbh = p.dtype == WA_DT_BF16 ? qbh : nullptr;
   }
   return off;
 }

@@ -35,6 +35,7 @@ struct FwdWorkspace {
                    // channels, fp32 path [ntok, HQ, K] float
   float *gsum;     // [ntok, HQ] running gate sum (log2 units)
   int *wide;       // [nseg, HQ] 1: the (segment, head) leaves the anchored operands' range
+  void *qbh;       // NULL, or the backward's half q_hat [HQ, ntok, K] (own-chunk anchor)
 };
 
 size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base);
@@ -63,10 +64,13 @@ struct BwdWorkspace {
   float *dq32, *dk_part, *dv_part;  // [ntok, HQ, K|V]: dq, each query head's dk and dv
   float *rows_ds, *cols_ds;         // [ntok, HQ] row and column sums of ds
   float *ctot;                      // [nseg*NCmax, HQ, K+1] chunk totals of dP and dGs
+  void *qbh;                        // bf16 inputs: [HQ, ntok, K] half q_hat for the MFMA kernels
 };
 size_t bwd_workspace_layout(const FwdProblem &p, BwdWorkspace *bw, char *base);
 hipError_t launch_attn_bwd(const BwdProblem &b, const FwdWorkspace &ws, const BwdWorkspace &bw,
                            hipStream_t st);
+hipError_t launch_attn_bwd_mfma(const BwdProblem &b, const FwdWorkspace &ws,
+                                const BwdWorkspace &bw, hipStream_t st);
 
 // Element types (the values of the public WA_BF16 / WA_F32 / WA_F16).
 enum { WA_DT_BF16 = 0, WA_DT_F32 = 1, WA_DT_F16 = 2 };

@@ -313,7 +313,8 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
     const TE *__restrict__ gs, const float *__restrict__ off, const float *__restrict__ anch,
     const float *__restrict__ off_s, TO *__restrict__ qh, TO *__restrict__ kt,
     float *__restrict__ gsum, const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ,
-    int H, int NCmax, float qscale, ChunkGrid cg, int *__restrict__ wide) {
+    int H, int NCmax, float qscale, ChunkGrid cg, int *__restrict__ wide,
+    _Float16 *__restrict__ qbh) {
   constexpr bool HM = std::is_same<TO, _Float16>::value;  // head-major rows with extras
   constexpr int KX = HM ? KD + 16 : KD;
   int hq, c;
@@ -358,6 +359,19 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
 #pragma unroll
         for (int j = 0; j < CPT; ++j) qo.v[j] = qv.v[j] * fast_exp2(p2[i].v[j] - RQ.v[j]) * qscale;
         storev<TO, CPT>(qh + (t * HQ + hq) * KD + CPT * cgi, qo);
+      }
+      if (HM && qbh != nullptr) {
+        // the backward's query operand: half, head-major [HQ, ntok, KD],
+        // anchored at the token's own chunk, q 2^(P2 - R_c) scale log2(e)
+        const FV<CPT> qv = loadv<TE, CPT>(q + (t * HQ + hq) * KD + CPT * cgi);
+        FV<CPT> qo;
+#pragma unroll
+        for (int j = 0; j < CPT; ++j) {
+          qo.v[j] = qv.v[j] * fast_exp2(p2[i].v[j] - A.v[j]) * qscale;
+          // room for the backward's factor of up to 2^4 on q_hat in half
+          out_of_range = out_of_range || !(fabsf(qo.v[j]) < 4096.f);
+        }
+        storev<_Float16, CPT>(qbh + ((int64_t)hq * ntok + t) * KD + CPT * cgi, qo);
       }
       const FV<CPT> kv = loadv<TE, CPT>(k + (t * H + h) * KD + CPT * cgi);
       FV<CPT> ko;
@@ -696,7 +710,8 @@ hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStrea
                      static_cast<const TE *>(p.q), static_cast<const TE *>(p.k),
                      static_cast<const TE *>(p.g), gs, ws.csum, ws.anch, ws.csum_s,
                      static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt), ws.gsum, p.cu, p.T,
-                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC, ws.wide);
+                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC, ws.wide,
+                     static_cast<_Float16 *>(ws.qbh));
   return hipGetLastError();
 }
 
@@ -777,6 +792,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
     ws->kt = kt;
     ws->gsum = reinterpret_cast<float *>(gsum);
     ws->wide = reinterpret_cast<int *>(wide);
+    ws->qbh = nullptr;  // the backward sets it to its own buffer
   }
   return off;
 }
