@@ -378,7 +378,8 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         ko.v[j] = kv.v[j] * fast_exp2(A.v[j] - p2[i].v[j]);
-        if (HM) out_of_range = out_of_range || !(fabsf(ko.v[j]) < 32768.f);
+        // the backward's key operand also takes chunk factors of up to 2^4
+        if (HM) out_of_range = out_of_range || !(fabsf(ko.v[j]) < (qbh != nullptr ? 4096.f : 32768.f));
       }
       storev<TO, CPT>(kt + (HM ? (hq * ntok + t) : (t * HQ + hq)) * KX + CPT * cgi, ko);
     }
