@@ -51,6 +51,11 @@ CASES = [
         g_mode="neg_softplus", g_std=0.05, g_scalar_std=0.01, sink=True, window=77, seed=89),
     cfg("f32_varlen_gqa2", 1, 0, 4, 2, 64, 64, torch.float32, nseq=5, len_lo=1, len_hi=200,
         seed=90),
+    # random-walk decay whose chunk-end sums rise by more than 4 log2 units
+    # between chunks in most heads: those heads leave the matrix-core kernels
+    # for the float32 ones (see test_rising_decay_case_leaves_the_fast_range)
+    cfg("bf16_T384_rising_decay_gate", 1, 384, 4, 2, 64, 64, torch.bfloat16, g_mode="normal",
+        g_std=0.07, g_scalar_std=0.01, seed=93),
     # the README's usage shape (B=2, T=1024, HQ=8, H=4, D=64)
     cfg("bf16_usage_shape_T1024", 2, 1024, 8, 4, 64, 64, torch.bfloat16, seed=91),
     # the long-context workload's head layout and decay at T=2048
@@ -103,3 +108,21 @@ def test_backward_deterministic(wa):
     b = grads_gpu(wa, x, dO)
     for n in a:
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_rising_decay_case_leaves_the_fast_range():
+    """Precondition of the rising-decay case: its chunk-end decay sums (log2
+    units, rounded as the anchors are) rise by more than 4 between an older
+    and a newer chunk in some head, which the matrix-core kernels hand to the
+    float32 kernels, while no chunk spans more than the operands' 8 log2
+    units (so the forward's own range flags stay clear)."""
+    c = [x for x in CASES if x.name == "bf16_T384_rising_decay_gate"][0]
+    g = W.make_prefill(c)["g"][0].double()
+    P2 = torch.cumsum(g, 0) * 1.4426950408889634
+    T = P2.shape[0]
+    ends = [min(64 * i + 63, T - 1) for i in range((T + 63) // 64)]
+    A = torch.stack([torch.round(P2[e]) for e in ends])
+    rise = max(float((A[i] - A[j]).max()) for i in range(len(ends)) for j in range(i + 1))
+    assert rise > 4
+    span = float((P2 - A.repeat_interleave(64, 0)[:T]).abs().max())
+    assert span < 7
