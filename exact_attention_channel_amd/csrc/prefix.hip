@@ -54,6 +54,22 @@ template <> __device__ __forceinline__ FV<8> loadv<float, 8>(const float *p) {
   const float4 x = reinterpret_cast<const float4 *>(p)[0], y = reinterpret_cast<const float4 *>(p)[1];
   return FV<8>{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
 }
+// The same 16 bytes kept raw (loaded early, converted where used).
+__device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
+template <typename TE, int N> __device__ __forceinline__ FV<N> fromraw(u32x4 w);
+template <> __device__ __forceinline__ FV<8> fromraw<bf16_t, 8>(u32x4 w) {
+  FV<8> r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    r.v[2 * j] = bf16_lo(w[j]);
+    r.v[2 * j + 1] = bf16_hi(w[j]);
+  }
+  return r;
+}
+template <> __device__ __forceinline__ FV<4> fromraw<float, 4>(u32x4 w) {
+  return FV<4>{{__uint_as_float(w[0]), __uint_as_float(w[1]), __uint_as_float(w[2]), __uint_as_float(w[3])}};
+}
+
 // N consecutive floats stored as N elements of TO (round to nearest even):
 // 16-bit types pack two per word, N = 8 is one 16-byte store, N = 4 one
 // 8-byte store.
@@ -307,7 +323,7 @@ struct ChunkScan {
 // is one contiguous block and the attention kernel's score product also
 // subtracts the row shift and the gate.  Float operands keep [ntok, HQ, KD].
 // grid (cg.size(), nseg), 256 threads; a thread owns CPT channels.
-template <typename TE, int KD, typename TO = typename OperandOf<TE>::type>
+template <typename TE, int KD, bool QBH, typename TO = typename OperandOf<TE>::type>
 __global__ __launch_bounds__(256) void k_prefill_operands(
     const TE *__restrict__ q, const TE *__restrict__ k, const TE *__restrict__ g,
     const TE *__restrict__ gs, const float *__restrict__ off, const float *__restrict__ anch,
@@ -332,6 +348,18 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   const int64_t cidx = (int64_t)s * NCmax + c;
   const FV<CPT> base = loadv<float, CPT>(off + (cidx * HQ + hq) * KD + CPT * cgi);
   const FV<CPT> A = loadv<float, CPT>(anch + (cidx * HQ + hq) * KD + CPT * cgi);
+  // the rows' keys (and queries, where this pass rescales them) load
+  // together with g, ahead of the in-chunk scan: one memory round trip
+  constexpr bool QL = !HM || QBH;  // queries needed below
+  u32x4 kin[CS::RPG], qin[CS::RPG];
+#pragma unroll
+  for (int i = 0; i < CS::RPG; ++i) {
+    const int r = grp * CS::RPG + i;
+    const int64_t t = r0 + r;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    kin[i] = r < nrow ? load16(k + (t * H + h) * KD + CPT * cgi) : z;
+    qin[i] = QL && r < nrow ? load16(q + (t * HQ + hq) * KD + CPT * cgi) : z;
+  }
   FV<CPT> p2[CS::RPG];
   CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
   // anchor of the query tile (its first chunk): q_hat = q 2^(P2 - RQ)
@@ -354,16 +382,16 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
         out_of_range = out_of_range || !(fabsf(A.v[j] - p2[i].v[j]) <= EMAX) ||
                        !(fabsf(p2[i].v[j] - RQ.v[j]) <= EMAX);
       if (!HM) {  // half operands: the attention kernel forms q_hat itself
-        const FV<CPT> qv = loadv<TE, CPT>(q + (t * HQ + hq) * KD + CPT * cgi);
+        const FV<CPT> qv = fromraw<TE, CPT>(qin[i]);
         FV<CPT> qo;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) qo.v[j] = qv.v[j] * fast_exp2(p2[i].v[j] - RQ.v[j]) * qscale;
         storev<TO, CPT>(qh + (t * HQ + hq) * KD + CPT * cgi, qo);
       }
-      if (HM && qbh != nullptr) {
+      if (HM && QBH) {
         // the backward's query operand: half, head-major [HQ, ntok, KD],
         // anchored at the token's own chunk, q 2^(P2 - R_c) scale log2(e)
-        const FV<CPT> qv = loadv<TE, CPT>(q + (t * HQ + hq) * KD + CPT * cgi);
+        const FV<CPT> qv = fromraw<TE, CPT>(qin[i]);
         FV<CPT> qo;
 #pragma unroll
         for (int j = 0; j < CPT; ++j) {
@@ -373,13 +401,13 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
         }
         storev<_Float16, CPT>(qbh + ((int64_t)hq * ntok + t) * KD + CPT * cgi, qo);
       }
-      const FV<CPT> kv = loadv<TE, CPT>(k + (t * H + h) * KD + CPT * cgi);
+      const FV<CPT> kv = fromraw<TE, CPT>(kin[i]);
       FV<CPT> ko;
 #pragma unroll
       for (int j = 0; j < CPT; ++j) {
         ko.v[j] = kv.v[j] * fast_exp2(A.v[j] - p2[i].v[j]);
         // the backward's key operand also takes chunk factors of up to 2^4
-        if (HM) out_of_range = out_of_range || !(fabsf(ko.v[j]) < (qbh != nullptr ? 4096.f : 32768.f));
+        if (HM) out_of_range = out_of_range || !(fabsf(ko.v[j]) < (QBH ? 4096.f : 32768.f));
       }
       storev<TO, CPT>(kt + (HM ? (hq * ntok + t) : (t * HQ + hq)) * KX + CPT * cgi, ko);
     }
@@ -707,12 +735,21 @@ hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStrea
   hipLaunchKernelGGL((k_chunk_scan<KD>), gridB, dim3(256), 0, st, ws.csum, ws.anch, ws.csum_s,
                      p.cu, p.T, (int)p.HQ, NCmax, gs != nullptr ? 1 : 0);
   const float qscale = p.scale * LOG2E;
-  hipLaunchKernelGGL((k_prefill_operands<TE, KD>), gridC, dim3(256), 0, st,
-                     static_cast<const TE *>(p.q), static_cast<const TE *>(p.k),
-                     static_cast<const TE *>(p.g), gs, ws.csum, ws.anch, ws.csum_s,
-                     static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt), ws.gsum, p.cu, p.T,
-                     p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC, ws.wide,
-                     static_cast<_Float16 *>(ws.qbh));
+  auto args = [&](auto kern) {
+    hipLaunchKernelGGL(kern, gridC, dim3(256), 0, st, static_cast<const TE *>(p.q),
+                       static_cast<const TE *>(p.k), static_cast<const TE *>(p.g), gs, ws.csum,
+                       ws.anch, ws.csum_s, static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt),
+                       ws.gsum, p.cu, p.T, p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC,
+                       ws.wide, static_cast<_Float16 *>(ws.qbh));
+  };
+  // the backward's half q_hat (bf16 inputs only) comes from its own instance
+  if constexpr (std::is_same<TE, bf16_t>::value) {
+    if (ws.qbh != nullptr) {
+      args(k_prefill_operands<TE, KD, true>);
+      return hipGetLastError();
+    }
+  }
+  args(k_prefill_operands<TE, KD, false>);
   return hipGetLastError();
 }
 
