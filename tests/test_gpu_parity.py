@@ -115,6 +115,12 @@ SMALL = [
         g_mode="neg_softplus", g_std=0.05, g_scalar_std=0.01, sink=True, seed=27),
     cfg("bf16_varlen_K64_V128_window200", 1, 0, 4, 1, 64, 128, torch.bfloat16, nseq=6,
         len_lo=100, len_hi=900, window=200, seed=28),
+    # long rows on few heads: many steady tile pairs per workgroup, windowed
+    # with gate and sink, and three long packed sequences
+    cfg("bf16_T1536_window700_gate_sink", 1, 1536, 4, 2, 64, 64, torch.bfloat16,
+        g_mode="neg_softplus", g_std=0.05, g_scalar_std=0.01, sink=True, window=700, seed=29),
+    cfg("bf16_varlen3_long_D128_sink", 1, 0, 2, 1, 128, 128, torch.bfloat16, nseq=3,
+        len_lo=600, len_hi=1500, sink=True, seed=30),
 ]
 
 
