@@ -58,21 +58,33 @@ __device__ void chunk_p2(const TE *__restrict__ g, const float *__restrict__ off
   __syncthreads();
 }
 
-// D_i = dO_i . o_i and, with a sink, exp(sink - lse_i) D_i: one wave per
-// (token, query head); grid ceil(ntok*HQ/4) x 256 threads.
+// D_i = dO_i . o_i and, with a sink, exp(sink - lse_i) D_i: a row of DV
+// elements is read by DV * sizeof(TE) / 16 threads, 16 bytes each; grid
+// ceil(ntok*HQ / rows per workgroup) x 256 threads.
 template <typename TE, int DV>
 __global__ __launch_bounds__(256) void k_bwd_rows(const TE *__restrict__ o, const TE *__restrict__ dO,
                                                   const float *__restrict__ lse,
                                                   const float *__restrict__ sink,
                                                   float *__restrict__ Dv, float *__restrict__ psD,
                                                   int64_t nrows, int HQ) {
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= nrows) return;
-  const int lane = threadIdx.x & 63;
+  constexpr int EPT = 16 / (int)sizeof(TE), TPR = DV / EPT, RPB = 256 / TPR;
+  const int64_t r = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int u = threadIdx.x % TPR;
   float acc = 0.f;
-  for (int c = lane; c < DV; c += 64) acc += Elem<TE>::ld(o + r * DV + c) * Elem<TE>::ld(dO + r * DV + c);
-  acc = wave_sum(acc);
-  if (lane == 0) {
+  if (r < nrows) {
+    const u32x4 a = *reinterpret_cast<const u32x4 *>(o + r * DV + EPT * u);
+    const u32x4 d = *reinterpret_cast<const u32x4 *>(dO + r * DV + EPT * u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (sizeof(TE) == 2)
+        acc += bf16_lo(a[i]) * bf16_lo(d[i]) + bf16_hi(a[i]) * bf16_hi(d[i]);
+      else
+        acc += __uint_as_float(a[i]) * __uint_as_float(d[i]);
+    }
+  }
+#pragma unroll
+  for (int w = TPR / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, TPR);
+  if (r < nrows && u == 0) {
     Dv[r] = acc;
     if (sink != nullptr) psD[r] = fast_exp2((sink[r % HQ] - lse[r]) * LOG2E) * acc;
   }
@@ -365,37 +377,54 @@ __global__ __launch_bounds__(256) void k_bwd_kv_sum(const float *__restrict__ dk
                                                     const float *__restrict__ dv_part,
                                                     TE *__restrict__ dk, TE *__restrict__ dv,
                                                     int64_t ntok, int HQ, int H) {
-  constexpr int DM = DK > DV ? DK : DV;
+  // four channels per thread: 16-byte loads of each query head's share
+  constexpr int DM = DK > DV ? DK : DV, Q = DM / 4;
   const int64_t x = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (x >= ntok * H * DM) return;
-  const int n = (int)(x % DM);
-  const int64_t th = x / DM;
+  if (x >= ntok * H * Q) return;
+  const int n = 4 * (int)(x % Q);
+  const int64_t th = x / Q;
   const int h = (int)(th % H);
   const int64_t t = th / H;
   const int G = HQ / H;
-  if (n < DK) {
-    float a = 0.f;
-    for (int u = 0; u < G; ++u) a += dk_part[(t * HQ + h * G + u) * DK + n];
-    Elem<TE>::st(dk + (t * H + h) * DK + n, a);
-  }
-  if (n < DV) {
-    float a = 0.f;
-    for (int u = 0; u < G; ++u) a += dv_part[(t * HQ + h * G + u) * DV + n];
-    Elem<TE>::st(dv + (t * H + h) * DV + n, a);
-  }
+  auto sum4 = [&](const float *part, int D, TE *out) {
+    f32x4 a = f32x4{};
+    for (int u = 0; u < G; ++u) a += *reinterpret_cast<const f32x4 *>(part + (t * HQ + h * G + u) * D + n);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Elem<TE>::st(out + (t * H + h) * D + n + e, a[e]);
+  };
+  if (n < DK) sum4(dk_part, DK, dk);
+  if (n < DV) sum4(dv_part, DV, dv);
 }
 
-// dsink[hq] = -sum over tokens of exp(sink - lse) D: one workgroup per head.
-__global__ __launch_bounds__(256) void k_bwd_dsink(const float *__restrict__ psD,
-                                                   float *__restrict__ dsink, int64_t ntok, int HQ) {
+// dsink[hq] = -sum over tokens of exp(sink - lse) D, in two fixed-order
+// passes: partial sums over blocks of DS_TOK tokens (grid blocks x HQ), then
+// their sum per head (one workgroup per head).
+constexpr int DS_TOK = 1024;
+__global__ __launch_bounds__(256) void k_bwd_dsink_part(const float *__restrict__ psD,
+                                                        float *__restrict__ part, int64_t ntok,
+                                                        int HQ) {
+  const int blk = blockIdx.x, hq = blockIdx.y;
+  const int64_t t0 = (int64_t)blk * DS_TOK;
+  const int64_t t1 = ntok - t0 < DS_TOK ? ntok : t0 + DS_TOK;
+  float acc = 0.f;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += 256) acc += psD[t * HQ + hq];
+  acc = wave_sum(acc);
+  __shared__ float w4[4];
+  if ((threadIdx.x & 63) == 0) w4[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) part[(int64_t)blk * HQ + hq] = w4[0] + w4[1] + w4[2] + w4[3];
+}
+
+__global__ __launch_bounds__(256) void k_bwd_dsink(const float *__restrict__ part,
+                                                   float *__restrict__ dsink, int nblk, int HQ) {
   const int hq = blockIdx.x;
   float acc = 0.f;
-  for (int64_t t = threadIdx.x; t < ntok; t += 256) acc += psD[t * HQ + hq];
+  for (int b = threadIdx.x; b < nblk; b += 256) acc += part[(int64_t)b * HQ + hq];
   acc = wave_sum(acc);
-  __shared__ float part[4];
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+  __shared__ float w4[4];
+  if ((threadIdx.x & 63) == 0) w4[threadIdx.x >> 6] = acc;
   __syncthreads();
-  if (threadIdx.x == 0) dsink[hq] = -(part[0] + part[1] + part[2] + part[3]);
+  if (threadIdx.x == 0) dsink[hq] = -(w4[0] + w4[1] + w4[2] + w4[3]);
 }
 
 template <typename TE, int DK, int DV>
@@ -408,7 +437,8 @@ hipError_t bwd_t(const BwdProblem &b, const FwdWorkspace &ws, const BwdWorkspace
   const TE *q = static_cast<const TE *>(p.q), *k = static_cast<const TE *>(p.k);
   const TE *v = static_cast<const TE *>(p.v), *g = static_cast<const TE *>(p.g);
   const TE *dO = static_cast<const TE *>(b.dO);
-  hipLaunchKernelGGL((k_bwd_rows<TE, DV>), dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, st,
+  constexpr int RPB = 256 / (DV * (int)sizeof(TE) / 16);  // rows per workgroup of k_bwd_rows
+  hipLaunchKernelGGL((k_bwd_rows<TE, DV>), dim3((unsigned)((nrows + RPB - 1) / RPB)), dim3(256), 0, st,
                      static_cast<const TE *>(b.o), dO, b.lse, p.sink, bw.Dv, bw.psD, nrows,
                      (int)p.HQ);
   // half-operand inputs: the matrix-core kernels take the pairs within the
@@ -436,13 +466,17 @@ hipError_t bwd_t(const BwdProblem &b, const FwdWorkspace &ws, const BwdWorkspace
                      static_cast<TE *>(b.dg), static_cast<TE *>(b.dgs), p.cu, p.T, (int)p.HQ,
                      (int)p.H, NCmax);
   constexpr int DM = DK > DV ? DK : DV;
-  const int64_t nkv = p.ntok * p.H * DM;
+  const int64_t nkv = p.ntok * p.H * (DM / 4);
   hipLaunchKernelGGL((k_bwd_kv_sum<TE, DK, DV>), dim3((unsigned)((nkv + 255) / 256)), dim3(256), 0,
                      st, bw.dk_part, bw.dv_part, static_cast<TE *>(b.dk), static_cast<TE *>(b.dv),
                      p.ntok, (int)p.HQ, (int)p.H);
-  if (b.dsink != nullptr)
-    hipLaunchKernelGGL(k_bwd_dsink, dim3((unsigned)p.HQ), dim3(256), 0, st, bw.psD, b.dsink,
-                       p.ntok, (int)p.HQ);
+  if (b.dsink != nullptr) {
+    const int nblk = (int)((p.ntok + DS_TOK - 1) / DS_TOK);
+    hipLaunchKernelGGL(k_bwd_dsink_part, dim3((unsigned)nblk, (unsigned)p.HQ), dim3(256), 0, st,
+                       bw.psD, bw.dsp, p.ntok, (int)p.HQ);
+    hipLaunchKernelGGL(k_bwd_dsink, dim3((unsigned)p.HQ), dim3(256), 0, st, bw.dsp, b.dsink, nblk,
+                       (int)p.HQ);
+  }
   return hipGetLastError();
 }
 
@@ -475,10 +509,11 @@ size_t bwd_workspace_layout(const FwdProblem &p, BwdWorkspace *bw, char *base) {
   float *rows_ds = take(sizeof(float) * nrows);
   float *cols_ds = take(sizeof(float) * nrows);
   float *ctot = take(sizeof(float) * p.nseg * NCmax * p.HQ * (p.K + 1));
+  float *dsp = take(sizeof(float) * ((p.ntok + DS_TOK - 1) / DS_TOK) * p.HQ);
   float *qbh = take(p.dtype == WA_DT_BF16 ? sizeof(uint16_t) * nrows * p.K : 0);
   if (bw) {
     bw->Dv = Dv; bw->psD = psD; bw->dq32 = dq32; bw->dk_part = dk_part; bw->dv_part = dv_part;
-    bw->rows_ds = rows_ds; bw->cols_ds = cols_ds; bw->ctot = ctot;
+    bw->rows_ds = rows_ds; bw->cols_ds = cols_ds; bw->ctot = ctot; bw->dsp = dsp;
     bw->qbh = p.dtype == WA_DT_BF16 ? qbh : nullptr;
   }
   return off;
