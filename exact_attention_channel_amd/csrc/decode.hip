@@ -29,12 +29,13 @@ extern template hipError_t launch_decode_cache<_Float16>(const DecodeParams &, i
 extern template hipError_t launch_decode_cache<float>(const DecodeParams &, int, int64_t, int64_t, const float *, void *, float *, int64_t, hipStream_t);
 
 // Splits of a call whose rows visit at most nchunks chunks: enough
-// workgroups for about eight full waves of three per CU.
+// workgroups for about four full waves of three per CU (four measured a
+// little faster than two, three, eight or sixteen on a 64-row 32K cache).
 void decode_split_plan(int64_t B, int64_t nchunks, int64_t HQ, int64_t H, int *nsplit,
                        int *chunks_per_split) {
   const int64_t NC = nchunks < 1 ? 1 : nchunks;
   const int64_t units = B * (HQ / dec::heads_per_block(HQ, H));
-  const int64_t target = 256 * 3 * 8;
+  const int64_t target = 256 * 3 * 4;
   int64_t ns = (target + units - 1) / units;
   ns = ns < 1 ? 1 : (ns > NC ? NC : ns);
   const int64_t cps = (NC + ns - 1) / ns;
@@ -49,7 +50,7 @@ void decode_split_plan(int64_t B, int64_t nchunks, int64_t HQ, int64_t H, int *n
 size_t decode_workspace_size(int64_t B, int64_t nchunks, int64_t HQ, int64_t H, int64_t V) {
   const int64_t NC = nchunks < 1 ? 1 : nchunks;
   const int64_t units = B * (HQ / dec::heads_per_block(HQ, H));
-  const int64_t target = 256 * 3 * 8;
+  const int64_t target = 256 * 3 * 4;
   int64_t ns = (target + units - 1) / units;
   ns = ns < 1 ? 1 : (ns > NC ? NC : ns);
   const size_t po = sizeof(float) * (size_t)(B * HQ * ns * V);
