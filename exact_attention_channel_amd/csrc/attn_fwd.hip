@@ -260,12 +260,15 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     float acc[CPL];
 #pragma unroll
     for (int c = 0; c < CPL; ++c) acc[c] = off[((cbase + cw) * HQ + hq) * DK + CPL * lane + c];
-    const bf16_t *g_b = g + (bos64 * HQ + hq) * DK + CPL * lane;
-    const bf16_t *q_b = q + (bos64 * HQ + hq) * DK + CPL * lane;
-    auto ld = [&](const bf16_t *base, int r) -> uint32_t {
-      if (r >= L) return 0u;
-      if (CPL == 2) return *reinterpret_cast<const uint32_t *>(base + (int64_t)r * qrow);
-      return base[(int64_t)r * qrow];
+    // buffer loads: the row offset is a scalar, and rows past the sequence
+    // read as zero without a branch per row
+    const int64_t ext = ((int64_t)(L - 1) * qrow + DK) * 2;
+    const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(g + uniform64((bos64 * HQ + hq) * DK), uniform64(ext));
+    const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + uniform64((bos64 * HQ + hq) * DK), uniform64(ext));
+    const __amdgpu_buffer_rsrc_t *g_b = &g_rs, *q_b = &q_rs;
+    auto ld = [&](const __amdgpu_buffer_rsrc_t *rs, int r) -> uint32_t {
+      if (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(*rs, 4 * lane, r * qrow * 2, 0);
+      return __builtin_amdgcn_raw_buffer_load_b16(*rs, 2 * lane, r * qrow * 2, 0);
     };
     uint32_t gp[32], gw[32], qw[32];  // g of the chunk's first half (second-half waves), g and q of the rows
 #pragma unroll
