@@ -13,7 +13,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = ["api.hip", "prefix.hip", "attn_fwd.hip", "attn_exact.hip", "attn_bwd.hip", "attn_bwd_mfma.hip", "decode.hip", "decode_cache_bf16.hip",
+SOURCES = ["api.hip", "prefix.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_bwd_mfma.hip", "decode.hip", "decode_cache_bf16.hip",
            "decode_cache_f16.hip", "decode_cache_f32.hip"]
 LIB = os.path.join(HERE, "libwallattn.so")
 ARCH = "gfx950"

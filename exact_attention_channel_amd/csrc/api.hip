@@ -120,10 +120,9 @@ int fwd_impl(int stages, const char *name, const void *q, const void *k, const v
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
   if (stages & STAGE_PREPARE) e = wa::launch_prefix_phases(p, ws, st);
+  // (the attention kernels also take the (segment, head) pairs the pre-pass
+  // flagged as out of the anchored operands' range, on their exact path)
   if (e == hipSuccess && (stages & STAGE_ATTEND)) e = wa::launch_attn_fwd(p, ws, st);
-  // (segment, head) pairs the pre-pass flagged as out of the anchored
-  // operands' range: exact kernel (its other workgroups return at once)
-  if (e == hipSuccess && (stages & STAGE_ATTEND)) e = wa::launch_attn_exact(p, ws, st);
   if (e != hipSuccess) return fail(WA_HIP_ERROR, "%s launch failed: %s", name, hipGetErrorString(e));
   return ok();
 }

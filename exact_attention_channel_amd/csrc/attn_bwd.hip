@@ -18,7 +18,7 @@
 // take float32 inputs and the (sequence, head) pairs the pre-pass flags as
 // outside the anchored operands' range: every (i, j) factor e^(P_in - P_jn)
 // is formed on its own as 2^(P2_in - P2_jn) (one exp2 per channel and pair,
-// the exact kernel's arithmetic), so they hold for every decay rate; float32
+// the forward's exact path's arithmetic), so they hold for every decay rate; float32
 // throughout, plain FMAs.
 //
 // Kernels: D and the sink terms per row; dq (a workgroup per query chunk,

@@ -37,10 +37,14 @@
 // Tiles outside the causal / window / sequence range are never visited and
 // only boundary tiles are masked element by element (the block-sparse idea
 // of FlexAttention's BlockMask, computed from indices instead of stored).
+// The workgroups of a (sequence, head) that the pre-pass flagged as outside
+// the anchored operands' range compute their rows with the exact path
+// (attn_exact.h) in the same LDS.
 #include <math.h>
 
 #include <type_traits>
 
+#include "attn_exact.h"
 #include "common.h"
 #include "launch.h"
 
@@ -141,8 +145,8 @@ __device__ __forceinline__ void vm_wait0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 template <int DK, int DV, bool HAS_GS>
 __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
-    const bf16_t *__restrict__ q, const bf16_t *__restrict__ g, const float *__restrict__ off,
-    const _Float16 *__restrict__ kt, const bf16_t *__restrict__ v,
+    const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ g,
+    const float *__restrict__ off, const _Float16 *__restrict__ kt, const bf16_t *__restrict__ v,
     const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ, int H, int nseg, int NCmax,
@@ -162,11 +166,14 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   // key tiles: rows of KRB bytes, 16-byte piece p of row r stored at piece
   // p ^ ((r >> 3) & 1) (rows r and r + 8 then read disjoint banks);
   // value tiles: rows of VRB bytes (2 DV data bytes, then padding)
+  // (separate LDS objects: the compiler tracks the LDS-direct loads per
+  // object, so a read of one buffer does not wait for loads into another)
   __shared__ __attribute__((aligned(16))) unsigned char K0[BK * KRB], K1[BK * KRB];
   __shared__ __attribute__((aligned(16))) unsigned char V0[BK * VRB], V1[BK * VRB];
   __shared__ __attribute__((aligned(16))) unsigned char Qs[QTILE * QSB];  // q_hat of the tile, half
   __shared__ __attribute__((aligned(16))) uint16_t Fq[NWV][DK];           // each wave's factors, half bits
   __shared__ int wg_ovf;
+  static_assert(QTILE * QSB >= exact::ExactLds<DK, DV>::BYTES, "the exact path fits in Qs");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index
@@ -185,9 +192,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   // sequence, sharing most of their key and value tiles in L2.
   const int seg = window > 0 ? rest / NQT : rest % nseg;
   const int I = NQT - 1 - (window > 0 ? rest % NQT : rest / nseg);
-  // a (segment, head) whose decay leaves the half operands' range is done by
-  // the exact kernel instead
-  if (__builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0) return;
+  const bool pair_wide = __builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0;
   int64_t bos64, eos64;
   segment_bounds(seg, T, cu, bos64, eos64);
   // sequence length (positions below are relative to bos), clamped to the
@@ -196,6 +201,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   const int L = (int)min(eos64 - bos64, (int64_t)NCmax * CHUNK);
   const int nqt = (L + QTILE - 1) / QTILE;
   if (I >= nqt) return;
+  if (pair_wide) {  // the decay leaves the half operands' range: exact rows
+    const float *off_s = off + ((int64_t)seg * NCmax * HQ + hq) * DK;
+    for (int c = I * (QTILE / CHUNK); c < min((I + 1) * (QTILE / CHUNK), (L + CHUNK - 1) / CHUNK); ++c)
+      exact::exact_chunk<bf16_t, DK, DV, HAS_GS>(q, k, v, g, off_s, gsum, sink, o, lse, bos64, L, hq, HQ, H,
+                                                 window, qscale, c, Qs);
+    return;
+  }
   const int h = hq / (HQ / H);
   const int i0 = I * QTILE;
   const int i_last = min(i0 + QTILE, L) - 1;
@@ -830,14 +842,17 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
 // workgroup, 4 threads per query row; thread `sub` owns channels n = 4e + sub.
 template <int DK, int DV, bool HAS_GS>
 __global__ __launch_bounds__(256) void k_attn_fwd_f32(
-    const float *__restrict__ qh, const float *__restrict__ kt, const float *__restrict__ v,
-    const float *__restrict__ anch, const float *__restrict__ gsum,
+    const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ off, const float *__restrict__ qh, const float *__restrict__ kt,
+    const float *__restrict__ v, const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, float *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int HQ, int H, int nseg, int NCmax, int NCH,
-    int64_t window, const int *__restrict__ wide) {
+    int64_t window, float qscale, const int *__restrict__ wide) {
   constexpr int QPT = DK / 4, VPT = DV / 4;
-  __shared__ float Ks[BN * DK];
-  __shared__ float Vs[BN * DV];
+  // keys then values; the exact path reuses the block
+  static_assert(4 * BN * (DK + DV) >= exact::ExactLds<DK, DV>::BYTES, "the exact path fits in the LDS block");
+  __shared__ __attribute__((aligned(16))) float KVs[BN * (DK + DV)];
+  float *const Ks = KVs, *const Vs = KVs + BN * DK;
   __shared__ float dL[DK];
   __shared__ float Gj[BN];
 
@@ -846,12 +861,19 @@ __global__ __launch_bounds__(256) void k_attn_fwd_f32(
   const int rest = blockIdx.x / HQ;
   const int seg = rest % nseg;
   const int c = NCH - 1 - rest / nseg;
-  if (__builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0) return;  // the exact kernel's
+  const bool pair_wide = __builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0;
   int64_t bos, eos;
   segment_bounds(seg, T, cu, bos, eos);
   const int64_t L = eos - bos;
   const int nch = (int)((L + CHUNK - 1) / CHUNK);
   if (c >= nch) return;
+  if (pair_wide) {  // the decay leaves the float operands' range: exact rows
+    exact::exact_chunk<float, DK, DV, HAS_GS>(q, k, v, g, off + ((int64_t)seg * NCmax * HQ + hq) * DK, gsum,
+                                              sink, o, lse, bos, (int)L, hq, HQ, H,
+                                              window > 0 && window < L ? (int)window : 0, qscale, c,
+                                              reinterpret_cast<unsigned char *>(KVs));
+    return;
+  }
   const int h = hq / (HQ / H);
   const int64_t i0 = bos + (int64_t)c * CHUNK;
   const int64_t i_last = min(i0 + CHUNK, eos) - 1;
@@ -944,8 +966,9 @@ hipError_t attn_bf16_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t 
   const dim3 grid((unsigned)(NQT * p.nseg * p.HQ));
   auto args = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(BfTile<DK, DV>::NTH), 0, st,
-                       static_cast<const bf16_t *>(p.q), static_cast<const bf16_t *>(p.g), ws.csum,
-                       static_cast<const _Float16 *>(ws.kt), static_cast<const bf16_t *>(p.v),
+                       static_cast<const bf16_t *>(p.q), static_cast<const bf16_t *>(p.k),
+                       static_cast<const bf16_t *>(p.g), ws.csum, static_cast<const _Float16 *>(ws.kt),
+                       static_cast<const bf16_t *>(p.v),
                        ws.anch, ws.gsum, p.sink, static_cast<bf16_t *>(p.o), p.lse, p.cu, p.T,
                        p.ntok, (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT,
                        (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0), p.scale * LOG2E,
@@ -963,10 +986,12 @@ hipError_t attn_f32_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t s
   const int NCmax = (int)((p.maxlen + CHUNK - 1) / CHUNK);
   const dim3 grid((unsigned)(NCmax * p.nseg * p.HQ));
   auto args = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const float *>(ws.qh),
-                       static_cast<const float *>(ws.kt), static_cast<const float *>(p.v),
-                       ws.anch, ws.gsum, p.sink, static_cast<float *>(p.o), p.lse, p.cu, p.T,
-                       (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NCmax, p.window, ws.wide);
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, static_cast<const float *>(p.q),
+                       static_cast<const float *>(p.k), static_cast<const float *>(p.g), ws.csum,
+                       static_cast<const float *>(ws.qh), static_cast<const float *>(ws.kt),
+                       static_cast<const float *>(p.v), ws.anch, ws.gsum, p.sink,
+                       static_cast<float *>(p.o), p.lse, p.cu, p.T, (int)p.HQ, (int)p.H,
+                       (int)p.nseg, NCmax, NCmax, p.window, p.scale * LOG2E, ws.wide);
   };
   if (p.g_scalar != nullptr)
     args(k_attn_fwd_f32<DK, DV, true>);

@@ -46,7 +46,6 @@ hipError_t launch_prefix_log2(const void *g, const void *gs, float *P2, float *G
                               const int32_t *cu, int64_t T, int64_t HQ, int64_t K, int64_t nseg,
                               int64_t maxlen, int dtype, void *ws, hipStream_t st);
 hipError_t launch_attn_fwd(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st);
-hipError_t launch_attn_exact(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t st);
 hipError_t launch_build_cache(const void *k, const float *P2, void *kt, float *rc, int64_t B,
                               int64_t T, int64_t HQ, int64_t H, int64_t K, int dtype,
                               int cache_dtype, hipStream_t st);

@@ -367,7 +367,7 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   const FV<CPT> RQ = loadv<float, CPT>(anch + (cq * HQ + hq) * KD + CPT * cgi);
   // Range of the anchored operands: the exponents of q_hat and k_tilde stay
   // within EMAX (and the half keys and gate sums below their limits), else
-  // the (segment, head) goes to the exact kernel.  The benchmark workloads
+  // the (segment, head) goes to the exact path.  The benchmark workloads
   // stay below 5.6; a decay sum changing by more than ~8 log2 units inside
   // one 64-token chunk does not.
   constexpr float EMAX = HM ? 8.f : 60.f;

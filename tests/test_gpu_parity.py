@@ -215,7 +215,7 @@ def test_prefill_gate_favouring_old_keys(wa, c):
 
 WIDE = [
     # decay sums that leave the anchored operands' range: the pre-pass sends
-    # these (sequence, head) pairs to the exact kernel
+    # these (sequence, head) pairs to the attention kernels' exact path
     cfg("bf16_T1024_strong_decay_gate_sink", 1, 1024, 4, 2, 128, 128, torch.bfloat16,
         g_mode="neg_softplus", g_std=0.5, g_scalar_std=0.01, sink=True, seed=61),
     cfg("bf16_T1024_strong_decay_window300", 1, 1024, 4, 2, 128, 128, torch.bfloat16,
@@ -229,7 +229,7 @@ WIDE = [
         len_lo=1, len_hi=400, fast_ch=8, fast_g=-2.0, window=90, sink=True, seed=65),
     cfg("f32_T1024_fast_channels_gate", 1, 1024, 2, 1, 64, 128, torch.float32, fast_ch=4,
         fast_g=-2.0, g_scalar_std=0.01, sink=True, seed=66),
-    # fp32 operands hold -0.5 softplus decays (no exact kernel)
+    # fp32 operands hold -0.5 softplus decays (no exact path)
     cfg("f32_T600_strong_decay", 1, 600, 2, 1, 128, 64, torch.float32, g_mode="neg_softplus",
         g_std=0.5, seed=67),
 ]

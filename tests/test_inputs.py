@@ -61,14 +61,14 @@ def operand_exponents(x, chunk=64):
 def test_benchmark_workloads_stay_in_the_half_operand_range():
     """The prefill workloads take the factorised path: both exponents within
     8 log2 units (the bound past which the pre-pass sends a (sequence, head)
-    to the exact kernel)."""
+    to the exact path)."""
     for c in (W.PREFILL_T1024_BF16, W.PREFILL_T8192_BF16, W.VARLEN_W2048_BF16):
         ek, eq = operand_exponents(W.make_prefill(c))
         assert ek <= 8 and eq <= 8, (c.name, ek, eq)
 
 
 def test_strong_decay_inputs_leave_the_half_operand_range():
-    """The GPU tests of the exact kernel use decays that overflow the half
+    """The GPU tests of the exact path use decays that overflow the half
     operands: g = -0.5 softplus(N) (about 37 log2 units per chunk) and
     channels decaying by 2 nats per token (185 per chunk; beyond float32 too)."""
     s = W.Prefill("s", 1, 1024, 4, 2, 128, 128, torch.bfloat16, g_mode="neg_softplus", g_std=0.5,
