@@ -119,11 +119,13 @@ template <int DK, int DV> struct BfTile {
   static constexpr int KX = DK + 16;           // channels of a key row: decayed + one extra block
   static constexpr int KRB = 2 * KX;           // bytes of a key row (global and LDS)
   static constexpr int KPR = KRB / 16;         // 16-byte pieces per key row
-  // bytes of a value row in LDS: 32 bytes of padding after the 2 DV data
-  // bytes (transpose reads of unpadded 256-byte rows, swizzled or not, run at
-  // about 60% of the padded rate)
-  static constexpr int VRB = 2 * DV + 32;
-  static constexpr int VPR = VRB / 16;         // 16-byte pieces per value row (the last two padding)
+  // bytes of a value row in LDS: 64 bytes of padding after the 2 DV data
+  // bytes.  A transpose read serves 32 lanes per pass, four consecutive rows
+  // x 64 bytes; with the row stride at 64 mod 256 bytes those four 64-byte
+  // pieces fall on disjoint banks (measured: no bank conflicts; a 32-byte
+  // pad left 24% of the LDS cycles in conflicts, unpadded rows ran at 60%)
+  static constexpr int VRB = 2 * DV + 64;
+  static constexpr int VPR = VRB / 16;         // 16-byte pieces per value row (the last four padding)
   static constexpr int QSB = 2 * DK + 16;      // LDS row stride of the query tile (bytes)
   static constexpr int NKI = BK * KRB / 1024;  // LDS-direct loads per key tile
   static constexpr int NVI = BK * VRB / 1024;  // LDS-direct loads per value tile
