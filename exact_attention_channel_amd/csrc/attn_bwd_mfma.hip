@@ -21,21 +21,24 @@
 // (sequence, head) and stops, and the float32 kernels, which run after
 // these and take every flagged pair, recompute that pair's gradients.
 //
-// Products are v_mfma_f32_32x32x16 (half for the rescaled q/k and ds, bf16
-// for P, V and dO).  P and ds never leave registers: a 32x32 score tile
-// holds, in lane l, column l%32 and the rows 8(r/4) + 4(l/32) + r%4 of its
-// 16 values r, which is the B operand of a product contracting over those
-// rows once the contraction index is taken in that order (two 16-row MFMAs
-// per tile).  The matching A operand -- dO^T, the rescaled q^T or k^T --
-// comes from row-major LDS tiles through ds_read_b64_tr_b16, which hands
-// lane i of each 16-lane group column i of the 4 x 16 block its lanes
-// address.  One workgroup per 64-key chunk walks the query chunks that see
-// it (dk, dv, column sums of ds); one per 64-row query chunk walks its key
-// chunks (dq, row sums).  Waves split a 64 x 64 block of pairs 2 x 2; the
-// next block's tiles are fetched into registers while the current block's
-// gradient products run.  The float32 finishing kernels of attn_bwd.hip (reverse
-// running sums, sums over query heads) complete the gradients.
+// Products run on the matrix cores (half for the rescaled q/k and ds, bf16
+// for P, V and dO).  P and ds never leave registers: a score tile holds, in
+// lane l, one column and a set of rows of its values, which is the B
+// operand of a product contracting over those rows once the contraction
+// index is taken in that order.  The matching A operand -- dO^T, the
+// rescaled q^T or k^T -- comes from row-major LDS tiles through
+// ds_read_b64_tr_b16, which hands lane i of each 16-lane group column i of
+// the 4 x 16 block its lanes address.  One workgroup per 64-key chunk walks
+// the query chunks that see it (dk, dv, column sums of ds: waves of 16 keys
+// on v_mfma_f32_16x16x32, the query blocks double-buffered in LDS through
+// LDS-direct loads); one per 64-row query chunk walks its key chunks (dq,
+// row sums: waves split a 64 x 64 block of pairs 2 x 2 on
+// v_mfma_f32_32x32x16, the next key chunk staged through registers).  The
+// float32 finishing kernels of attn_bwd.hip (reverse running sums, sums over
+// query heads) complete the gradients.
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "launch.h"
@@ -110,10 +113,17 @@ __device__ void chunk_p2(const bf16_t *__restrict__ g, const float *__restrict__
                          int nrow, int HQ, int hq, float *P2s, float *tot) {
   constexpr int NSEG = 256 / DK, RPS = XC / NSEG;
   const int n = threadIdx.x % DK, sg = threadIdx.x / DK;
+  float x[RPS];  // the segment's rows, loaded together
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) {
+    const int r = sg * RPS + i;
+    x[i] = r < nrow ? bf16_to_f32(g[((r0 + r) * HQ + hq) * DK + n]) : 0.f;
+  }
   float acc = 0.f;
-  for (int r = sg * RPS; r < sg * RPS + RPS; ++r) {
-    acc += r < nrow ? bf16_to_f32(g[((r0 + r) * HQ + hq) * DK + n]) : 0.f;
-    P2s[r * DK + n] = acc;
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) {
+    acc += x[i];
+    P2s[(sg * RPS + i) * DK + n] = acc;
   }
   tot[sg * DK + n] = acc;
   __syncthreads();
@@ -150,36 +160,122 @@ __device__ __forceinline__ bool factors_in_range(const float *a, const float *b)
 }
 
 // ---------------------------------------------------------------------------
-// dk, dv (each query head's share) and the column sums of ds.
-// grid (NCmax*HQ, nseg): x = key chunk (longest first) * HQ + head, y = segment.
-// Wave w: query rows 32 (w&1), keys 32 (w>>1) of each 64 x 64 block.
+// dk, dv (each query head's share) and the column sums of ds, with waves of
+// 16 keys.  grid (NCmax*HQ, nseg): x = key chunk (longest first) * HQ + head,
+// y = segment.  Wave w owns keys 16 w .. 16 w + 15 of the chunk over all 64
+// rows of each query block, on v_mfma_f32_16x16x32 (A lane l: row l%16,
+// k 8(l/16)..+7; B lane l: column l%16, same k; result lane l: column l%16,
+// rows 4(l/16) + r):
+//   S[q, key]  = Q''[q] . k_tilde[key],   Q'' = q_hat 2^(A_I - R_J)
+//   dP[q, key] = dO . v
+//   dV^T[ch, key] += dO^T P,  dK^T[ch, key] += Q''^T ds
+// The last two contract over the block's rows in the order of the result
+// tiles' values (two 16-row tiles per 32-row step), their A operands read
+// transposed from LDS.  The q_hat and dO blocks and the rows' statistics go
+// to LDS through LDS-direct loads, double-buffered: the next block loads
+// while the current one is computed.  Each thread then scales the q_hat
+// pieces it loaded by their channels' factors (one 8-channel group per
+// thread, whose anchors it loads itself), so no extra barrier is needed.
+// Half the accumulators of 32-key waves, no reduction over row halves.
+template <int D> __device__ __forceinline__ int qswz(int r) {
+  // 16-byte piece p of row r of an unpadded [64][D] tile sits at p ^ qswz(r):
+  // the 16-byte row reads (16 consecutive rows, one piece) and the transposed
+  // reads (8 consecutive rows from a multiple of 8, two pieces) hit distinct
+  // banks
+  return D == 128 ? ((r & 7) << 1) | ((r >> 3) & 1) : (((r >> 1) & 3) << 1) | ((r >> 3) & 1);
+}
+template <int D> __device__ __forceinline__ int qpiece(int r, int p) { return r * D + 8 * (p ^ qswz<D>(r)); }
+
+template <typename T> struct Mfma16;
+template <> struct Mfma16<_Float16> {
+  typedef f16x8 V;
+  static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct Mfma16<bf16_t> {
+  typedef bf16x8 V;
+  static __device__ __forceinline__ f32x4 run(V a, V b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+// A operand of a 16x16x32 product that contracts over the rows of a swizzled
+// LDS tile M [64][D]: output rows (channels) c0 .. c0+15, contraction rows
+// x0 + 4 (lane/16) + {0..3} and x0 + 16 + 4 (lane/16) + {0..3}.
+template <typename T, int D>
+__device__ __forceinline__ typename Mfma16<T>::V tr16_operand(const T *M, int x0, int c0, int lane) {
+  const int row = x0 + 4 * (lane >> 4) + ((lane >> 2) & 3);
+  const int col = c0 + 4 * (lane & 3);
+  const s16x4 lo = tr16(M + qpiece<D>(row, col >> 3) + (col & 7));
+  const s16x4 hi = tr16(M + qpiece<D>(row + 16, col >> 3) + (col & 7));
+  return __builtin_bit_cast(typename Mfma16<T>::V, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, int64_t bytes) {
+  const int n = bytes > 0x7fffffff ? 0x7fffffff : (bytes < 0 ? 0 : (int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, n, 0x00020000);
+}
+// LDS-direct loads: lane l writes LDS bytes dst + 16 l .. + 15 (dst + 4 l .. + 3) from its
+// buffer offset (zeros past the resource's extent); counted by vmcnt.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, void *dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (lds_void *)(__attribute__((address_space(3))) unsigned char *)dst, 16, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, void *dst, int voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (lds_void *)(__attribute__((address_space(3))) unsigned char *)dst, 4, voff, 0, 0, 0);
+}
+__device__ __forceinline__ void vm_wait0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
+
+// Running decay sums (log2 units) of channels c0 .. c0 + NCP - 1 of one
+// chunk's rows into P2s [XC][NCP].
+template <int NCP>
+__device__ void part_p2(const bf16_t *__restrict__ g, const float *__restrict__ off_c, int64_t r0,
+                        int nrow, int HQ, int hq, int DKg, int c0, float *P2s, float *tot) {
+  constexpr int NSEG = 256 / NCP, RPS = XC / NSEG;
+  const int n = threadIdx.x % NCP, sg = threadIdx.x / NCP;
+  float x[RPS];  // the segment's rows, loaded together
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) {
+    const int r = sg * RPS + i;
+    x[i] = r < nrow ? bf16_to_f32(g[((r0 + r) * HQ + hq) * DKg + c0 + n]) : 0.f;
+  }
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPS; ++i) {
+    acc += x[i];
+    P2s[(sg * RPS + i) * NCP + n] = acc;
+  }
+  tot[sg * NCP + n] = acc;
+  __syncthreads();
+  float base = off_c[c0 + n];
+  for (int q = 0; q < sg; ++q) base += tot[q * NCP + n];
+  for (int r = sg * RPS; r < sg * RPS + RPS; ++r) P2s[r * NCP + n] = (base + P2s[r * NCP + n]) * LOG2E;
+  __syncthreads();
+}
+
 template <int DK, int DV, bool HAS_GS>
-__global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mfma(
+__global__ __launch_bounds__(256, 2) void k_bwd_dkdv_w16(
     const _Float16 *__restrict__ kt, const _Float16 *__restrict__ qbh, const bf16_t *__restrict__ v,
     const bf16_t *__restrict__ dO, const bf16_t *__restrict__ g, const float *__restrict__ off,
     const float *__restrict__ anch, const float *__restrict__ gsum, const float *__restrict__ lse,
     const float *__restrict__ Dv, int *__restrict__ wide, float *__restrict__ dk_part,
     float *__restrict__ dv_part, float *__restrict__ cols_ds, const int32_t *__restrict__ cu,
     int64_t T, int64_t ntok, int HQ, int H, int NCmax, int window) {
-  constexpr int KS = DK + 8, VS = DV + 8;  // padded LDS row strides (elements)
-  constexpr int KX = DK + 16;              // k_tilde row in the forward workspace
-  constexpr int TK = DK / 32, TV = DV / 32;
-  constexpr int QI = XC * DK / 8 / 256, OI = XC * DV / 8 / 256;  // 16-byte items per thread
-  constexpr int O_KT = 0, O_VS = O_KT + XC * KS * 2, O_QP = O_VS + XC * VS * 2,
-                O_OS = O_QP + XC * KS * 2, O_LOOP = O_OS + XC * VS * 2;
-  // epilogue: the two row halves' partial sums; P2 of the key chunk then
-  // takes the place of dv's
-  constexpr int XKS = DK + 1, XVS = DV + 1;
-  constexpr int E_XV = XC * XKS * 4, E_P2 = E_XV;
-  constexpr int E_END = E_XV + (XVS > DK ? XC * XVS * 4 : XC * DK * 4);
-  constexpr int LDS_BYTES = O_LOOP > E_END ? O_LOOP : E_END;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) float Rj[DK], Li[XC], Di[XC], Gi[XC], Gj[XC], csh[2][XC];
+  constexpr int KX = DK + 16;                       // k_tilde row in the forward workspace
+  constexpr int QB = XC * DK * 2, OB = XC * DV * 2;  // bytes of a q_hat / dO block
+  constexpr int NQD = QB / 1024, NOD = OB / 1024;    // 1-KiB LDS-direct loads per block
+  constexpr int NSK = DK / 32, NSV = DV / 32;        // 32-channel steps of S and dP
+  constexpr int NCK = DK / 16, NCV = DV / 16;        // 16-channel blocks of dK^T and dV^T
+  constexpr int SA = 3 * XC;                         // statistics: L, D, G of the rows
+  constexpr int NCP = QB / (XC * 4) < 64 ? QB / (XC * 4) : 64;  // channels per epilogue pass
+  static_assert(NQD % 4 == 0 && NOD % 4 == 0, "a block is a multiple of 4 KiB");
+  __shared__ __attribute__((aligned(16))) unsigned char Qb0[QB], Qb1[QB];
+  __shared__ __attribute__((aligned(16))) unsigned char Ob0[OB], Ob1[OB];
+  __shared__ __attribute__((aligned(16))) float St0[SA], St1[SA];
+  __shared__ __attribute__((aligned(16))) float Rj[DK], Gj[XC];
   __shared__ float tot[256];
-  _Float16 *Kt = reinterpret_cast<_Float16 *>(lds + O_KT);
-  bf16_t *Vs = reinterpret_cast<bf16_t *>(lds + O_VS);
-  _Float16 *Qp = reinterpret_cast<_Float16 *>(lds + O_QP);
-  bf16_t *Os = reinterpret_cast<bf16_t *>(lds + O_OS);
 
   const int hq = blockIdx.x % HQ, J = blockIdx.x / HQ, seg = blockIdx.y;
   if (__builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0) return;
@@ -190,206 +286,226 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_mfma(
   if (J >= nch) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = w & 1, kb = w >> 1;
+  const int c16 = lane & 15, gq = lane >> 4;
   const int h = hq / (HQ / H);
   const int j0 = J * XC, nk = min(XC, L - j0);
   const int64_t cbase = (int64_t)seg * NCmax;
-  const float *anch_h = anch + (int64_t)hq * DK;  // chunk c: + c*HQ*DK
+  const int kw = 16 * w + c16;  // this lane's key in the chunk
+  const bool kok = kw < nk;
 
-  // the key chunk: k_tilde, v, anchors, gate sums
+  // the wave's keys and values as B operands (channels 32 s + 8 (lane/16) ..)
+  f16x8 kr[NSK];
+  bf16x8 vr[NSV];
 #pragma unroll
-  for (int u = 0; u < QI; ++u) {
-    const int x = tid + 256 * u, r = x / (DK / 8), p = x % (DK / 8);
-    *reinterpret_cast<u32x4 *>(Kt + r * KS + 8 * p) =
-        ld16(kt + ((int64_t)hq * ntok + bos + j0 + r) * KX + 8 * p, r < nk);
-  }
+  for (int s = 0; s < NSK; ++s)
+    kr[s] = __builtin_bit_cast(f16x8, ld16(kt + ((int64_t)hq * ntok + bos + j0 + kw) * KX + 32 * s + 8 * gq, kok));
 #pragma unroll
-  for (int u = 0; u < OI; ++u) {
-    const int x = tid + 256 * u, r = x / (DV / 8), p = x % (DV / 8);
-    *reinterpret_cast<u32x4 *>(Vs + r * VS + 8 * p) =
-        ld16(v + ((bos + j0 + r) * H + h) * DV + 8 * p, r < nk);
-  }
-  if (tid < DK) Rj[tid] = anch_h[(cbase + J) * HQ * DK + tid];
+  for (int s = 0; s < NSV; ++s)
+    vr[s] = __builtin_bit_cast(bf16x8, ld16(v + ((bos + j0 + kw) * H + h) * DV + 32 * s + 8 * gq, kok));
+  if (tid < DK) Rj[tid] = anch[((cbase + J) * HQ + hq) * DK + tid];
   if (tid < XC) Gj[tid] = (HAS_GS && tid < nk) ? gsum[(bos + j0 + tid) * HQ + hq] : 0.f;
-  __syncthreads();
+  __syncthreads();  // Rj and Gj are read by every wave from the first block on
 
-  // this thread's staging items: channels 8 pq .. 8 pq + 7 of rows rq + stride u
-  const int pq = tid % (DK / 8), po = tid % (DV / 8);
-  float rjw[DK / 64];
+  // sources of the query blocks (rows relative to bos; rows past L read zero)
+  const __amdgpu_buffer_rsrc_t q_rs =
+      make_rsrc(qbh + uniform64(((int64_t)hq * ntok + bos) * DK), uniform64((int64_t)L * DK * 2));
+  const __amdgpu_buffer_rsrc_t o_rs =
+      make_rsrc(dO + uniform64((bos * HQ + hq) * DV), uniform64(((int64_t)(L - 1) * HQ * DV + DV) * 2));
+  const int64_t srow = ((int64_t)(L - 1) * HQ + 1) * 4;
+  const __amdgpu_buffer_rsrc_t l_rs = make_rsrc(lse + uniform64(bos * HQ + hq), uniform64(srow));
+  const __amdgpu_buffer_rsrc_t d_rs = make_rsrc(Dv + uniform64(bos * HQ + hq), uniform64(srow));
+  const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(gsum + uniform64(bos * HQ + hq), uniform64(HAS_GS ? srow : 0));
+  // block I into a buffer: load m of a tile by wave m % 4, lane l filling
+  // LDS piece 64 m + l (row r, piece pp) from piece pp ^ qswz(r) of row r;
+  // the statistics by one wave each (4 bytes a lane)
+  auto issue = [&](int I, unsigned char *Qb, unsigned char *Ob, float *St) {
+    const int i0 = I * XC;
 #pragma unroll
-  for (int c = 0; c < DK / 64; ++c) rjw[c] = Rj[lane + 64 * c];
-
-  // prefetch registers of the next query chunk
-  u32x4 fq[QI], fo[OI];
-  float fe8[8], faw[DK / 64], frow[3] = {0.f, 0.f, 0.f};
-  auto fetch = [&](int I) {
-    const int i0 = I * XC, nq = min(XC, L - i0);
-#pragma unroll
-    for (int u = 0; u < QI; ++u) {
-      const int r = (tid + 256 * u) / (DK / 8);
-      fq[u] = ld16(qbh + ((int64_t)hq * ntok + bos + i0 + r) * DK + 8 * pq, r < nq);
+    for (int mm = 0; mm < NQD / 4; ++mm) {
+      const int m = w + 4 * mm, gi = 64 * m + lane, r = gi / (DK / 8), pp = gi % (DK / 8);
+      dma16(q_rs, Qb + 1024 * m, ((i0 + r) * DK + 8 * (pp ^ qswz<DK>(r))) * 2);
     }
 #pragma unroll
-    for (int u = 0; u < OI; ++u) {
-      const int r = (tid + 256 * u) / (DV / 8);
-      fo[u] = ld16(dO + ((bos + i0 + r) * HQ + hq) * DV + 8 * po, r < nq);
+    for (int mm = 0; mm < NOD / 4; ++mm) {
+      const int m = w + 4 * mm, gi = 64 * m + lane, r = gi / (DV / 8), pp = gi % (DV / 8);
+      dma16(o_rs, Ob + 1024 * m, ((i0 + r) * HQ * DV + 8 * (pp ^ qswz<DV>(r))) * 2);
     }
-    const float *aI = anch_h + (cbase + I) * HQ * DK;
-    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(aI + 8 * pq);
-    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(aI + 8 * pq + 4);
+    if (w == 0) dma4(l_rs, St, (i0 + lane) * HQ * 4);
+    if (w == 1) dma4(d_rs, St + XC, (i0 + lane) * HQ * 4);
+    if (HAS_GS && w == 2) dma4(g_rs, St + 2 * XC, (i0 + lane) * HQ * 4);
+  };
+  // This thread's q_hat pieces (loads m = w + 4 mm) all hold one 8-channel
+  // group: their rows agree mod 16, so the swizzle maps them to one piece
+  // index.  Its anchors are loaded with each block, the key chunk's kept.
+  const int lpq = (lane % (DK / 8)) ^ qswz<DK>((64 * w + lane) / (DK / 8));
+  f32x4 aq0, aq1;
+  float ac[DK / 64];
+  auto load_anchors = [&](int I) {
+    const float *aI = anch + ((cbase + I) * HQ + hq) * DK;
+    aq0 = *reinterpret_cast<const f32x4 *>(aI + 8 * lpq);
+    aq1 = *reinterpret_cast<const f32x4 *>(aI + 8 * lpq + 4);
+#pragma unroll
+    for (int c = 0; c < DK / 64; ++c) ac[c] = aI[lane + 64 * c];
+  };
+  // once the block's loads are complete: whether every chunk factor is in
+  // range (the same answer in every wave), and this thread's q_hat pieces
+  // times 2^(A_I - R_J)
+  auto scale_own = [&](unsigned char *Qb) -> bool {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < DK / 64; ++c) mx = fmaxf(mx, ac[c] - Rj[lane + 64 * c]);
+    if (wave_max(mx) > 4.f) return false;
+    const f32x4 r0 = *reinterpret_cast<const f32x4 *>(Rj + 8 * lpq);
+    const f32x4 r1 = *reinterpret_cast<const f32x4 *>(Rj + 8 * lpq + 4);
+    f16x8 fac;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      fe8[e] = a0[e] - Rj[8 * pq + e];
-      fe8[4 + e] = a1[e] - Rj[8 * pq + 4 + e];
+      fac[e] = (_Float16)__builtin_amdgcn_ldexpf(1.f, (int)(aq0[e] - r0[e]));
+      fac[4 + e] = (_Float16)__builtin_amdgcn_ldexpf(1.f, (int)(aq1[e] - r1[e]));
     }
 #pragma unroll
-    for (int c = 0; c < DK / 64; ++c) faw[c] = aI[lane + 64 * c];
-    if (tid < XC) {
-      const bool ok = tid < nq;
-      const int64_t t = bos + i0 + tid;
-      frow[0] = ok ? lse[t * HQ + hq] * LOG2E : 0.f;
-      frow[1] = ok ? Dv[t * HQ + hq] : 0.f;
-      frow[2] = (HAS_GS && ok) ? gsum[t * HQ + hq] : 0.f;
+    for (int mm = 0; mm < NQD / 4; ++mm) {
+      f16x8 *pc = reinterpret_cast<f16x8 *>(Qb + 1024 * (w + 4 * mm) + 16 * lane);
+      *pc = *pc * fac;
     }
-  };
-  // registers -> LDS: Q'' = q_hat 2^(A_I - R_J), dO, row statistics; false
-  // (nothing written) when a chunk factor is out of range
-  auto commit = [&]() {
-    if (!factors_in_range<DK>(faw, rjw)) return false;
-#pragma unroll
-    for (int u = 0; u < QI; ++u) {
-      const int r = (tid + 256 * u) / (DK / 8);
-      *reinterpret_cast<u32x4 *>(Qp + r * KS + 8 * pq) = rescale8(fq[u], fe8);
-    }
-#pragma unroll
-    for (int u = 0; u < OI; ++u) {
-      const int r = (tid + 256 * u) / (DV / 8);
-      *reinterpret_cast<u32x4 *>(Os + r * VS + 8 * po) = fo[u];
-    }
-    if (tid < XC) { Li[tid] = frow[0]; Di[tid] = frow[1]; Gi[tid] = frow[2]; }
     return true;
   };
 
-  f32x16 dVa[TV], dKa[TK];
+  f32x4 dVa[NCV], dKa[NCK];
 #pragma unroll
-  for (int t = 0; t < TV; ++t) dVa[t] = f32x16{};
+  for (int t = 0; t < NCV; ++t) dVa[t] = f32x4{};
 #pragma unroll
-  for (int t = 0; t < TK; ++t) dKa[t] = f32x16{};
+  for (int t = 0; t < NCK; ++t) dKa[t] = f32x4{};
   float csum = 0.f;
-
   const int Ihi = window > 0 ? min(nch - 1, (j0 + XC - 1 + window - 1) / XC) : nch - 1;
-  fetch(J);
-  if (!commit()) {
-    if (tid == 0) wide[seg * HQ + hq] = 1;
-    return;
-  }
-  __syncthreads();
-  const int key = 32 * kb + (lane & 31);  // this lane's key in the chunk
-  const int jrel = j0 + key;
-  const float gk = Gj[key];
-  for (int I = J; I <= Ihi; ++I) {
+  const int jrel = j0 + kw;
+
+  // one query block from buffer P; false (nothing issued) when a chunk
+  // factor is out of range -- every wave reads the same anchors and agrees
+  auto block = [&](auto par_c, int I) {
+    constexpr int P = decltype(par_c)::value;
+    const unsigned char *const Qb = P ? Qb1 : Qb0;
+    const unsigned char *const Ob = P ? Ob1 : Ob0;
+    const float *const St = P ? St1 : St0;
+    if (I < Ihi) {
+      issue(I + 1, P ? Qb0 : Qb1, P ? Ob0 : Ob1, P ? St0 : St1);
+      load_anchors(I + 1);
+    }
+    const _Float16 *Qh = reinterpret_cast<const _Float16 *>(Qb);
+    const bf16_t *Oh = reinterpret_cast<const bf16_t *>(Ob);
+    // S = Q'' k_tilde^T and dP = dO v^T: four 16-row tiles
+    f32x4 S[4], dPt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) S[t] = dPt[t] = f32x4{};
+#pragma unroll
+    for (int s = 0; s < NSK; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        S[t] = Mfma16<_Float16>::run(
+            *reinterpret_cast<const f16x8 *>(Qh + qpiece<DK>(16 * t + c16, 4 * s + gq)), kr[s], S[t]);
+#pragma unroll
+    for (int s = 0; s < NSV; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dPt[t] = Mfma16<bf16_t>::run(
+            *reinterpret_cast<const bf16x8 *>(Oh + qpiece<DV>(16 * t + c16, 4 * s + gq)), vr[s], dPt[t]);
+    // probabilities and ds: lane's key kw, rows 16 t + 4 (lane/16) + e
     const int i0 = I * XC, nq = min(XC, L - i0);
-    // S = Q'' K^T, dP = dO V^T for rows 32 qb, keys 32 kb
-    f32x16 S = f32x16{}, dP = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks)
-      S = Mfma<_Float16>::run(row_operand(Qp + 32 * qb * KS, KS, 16 * ks, lane),
-                              row_operand(Kt + 32 * kb * KS, KS, 16 * ks, lane), S);
-#pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks)
-      dP = Mfma<bf16_t>::run(row_operand(Os + 32 * qb * VS, VS, 16 * ks, lane),
-                             row_operand(Vs + 32 * kb * VS, VS, 16 * ks, lane), dP);
-    // every pair of the block visible: full chunks, strictly below the
-    // diagonal, inside the window
     const bool full = nq == XC && nk == XC && I > J && !(window > 0 && i0 + XC - 1 - j0 >= window);
+    const float gk = Gj[kw];
     float pv[16], dsv[16];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int n0 = 32 * qb + 8 * a + 4 * (lane >> 5);  // rows n0 .. n0+3 (values 4a .. 4a+3)
-      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(Li + n0);
-      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(Di + n0);
+    for (int t = 0; t < 4; ++t) {
+      const int n0 = 16 * t + 4 * gq;
+      const f32x4 l4 = *reinterpret_cast<const f32x4 *>(St + n0);
+      const f32x4 d4 = *reinterpret_cast<const f32x4 *>(St + XC + n0);
       f32x4 g4 = f32x4{};
-      if (HAS_GS) g4 = *reinterpret_cast<const f32x4 *>(Gi + n0);
+      if (HAS_GS) g4 = *reinterpret_cast<const f32x4 *>(St + 2 * XC + n0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 4 * a + e;
-        float s2 = S[r];
+        float s2 = S[t][e];
         if (HAS_GS) s2 += g4[e] - gk;
         bool ok = true;
         if (!full) {
           const int irel = i0 + n0 + e;
-          ok = n0 + e < nq && key < nk && jrel <= irel && !(window > 0 && irel - jrel >= window);
+          ok = n0 + e < nq && kok && jrel <= irel && !(window > 0 && irel - jrel >= window);
         }
-        const float p = ok ? fast_exp2(s2 - l4[e]) : 0.f;
-        const float ds = p * (dP[r] - d4[e]);
-        pv[r] = p;
-        dsv[r] = ds;
+        const float p = ok ? fast_exp2(s2 - l4[e] * LOG2E) : 0.f;
+        const float ds = p * (dPt[t][e] - d4[e]);
+        pv[4 * t + e] = p;
+        dsv[4 * t + e] = ds;
         csum += ds;
       }
     }
-    // dV^T += dO^T P and dK^T += Q''^T ds, contracting over the 32 rows
+    // dV^T += dO^T P, dK^T += Q''^T ds over two 32-row steps
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const bf16x8 pb = pack_b(pv + 8 * m);
+    for (int u = 0; u < 2; ++u) {
+      const bf16x8 pb = pack_b(pv + 8 * u);
+      const f16x8 db = pack_h(dsv + 8 * u);
 #pragma unroll
-      for (int t = 0; t < TV; ++t)
-        dVa[t] = Mfma<bf16_t>::run(tr_operand(Os, VS, 32 * qb + 16 * m, 32 * t, lane), pb, dVa[t]);
-      const f16x8 db = pack_h(dsv + 8 * m);
+      for (int cb = 0; cb < NCV; ++cb)
+        dVa[cb] = Mfma16<bf16_t>::run(tr16_operand<bf16_t, DV>(Oh, 32 * u, 16 * cb, lane), pb, dVa[cb]);
 #pragma unroll
-      for (int t = 0; t < TK; ++t)
-        dKa[t] = Mfma<_Float16>::run(tr_operand(Qp, KS, 32 * qb + 16 * m, 32 * t, lane), db, dKa[t]);
+      for (int cb = 0; cb < NCK; ++cb)
+        dKa[cb] = Mfma16<_Float16>::run(tr16_operand<_Float16, DK>(Qh, 32 * u, 16 * cb, lane), db, dKa[cb]);
     }
-    __syncthreads();  // the block's tiles are consumed
-    if (I < Ihi) {
-      fetch(I + 1);
-      if (!commit()) {
-        if (tid == 0) wide[seg * HQ + hq] = 1;
-        return;
-      }
-      __syncthreads();
-    }
+    return true;
+  };
+
+  // blocks alternate between the two buffers; after each block, its
+  // successor's loads are waited for and scaled, then one barrier
+  issue(J, Qb0, Ob0, St0);
+  load_anchors(J);
+  vm_wait0();
+  bool in_range = scale_own(Qb0);
+  __syncthreads();
+  for (int I = J; in_range;) {
+    block(std::integral_constant<int, 0>{}, I);
+    if (I == Ihi) break;
+    ++I;
+    vm_wait0();
+    in_range = scale_own(Qb1);
+    __syncthreads();
+    if (!in_range) break;
+    block(std::integral_constant<int, 1>{}, I);
+    if (I == Ihi) break;
+    ++I;
+    vm_wait0();
+    in_range = scale_own(Qb0);
+    __syncthreads();
+  }
+  if (!in_range) {  // a chunk factor above 2^4: the float32 kernels take the pair
+    if (tid == 0) wide[seg * HQ + hq] = 1;
+    return;
   }
 
-  // sum the two row halves' partials in LDS ([key][channel]), then write out
-  float *Xk = reinterpret_cast<float *>(lds);
-  float *Xv = reinterpret_cast<float *>(lds + E_XV);
-  float *P2s = reinterpret_cast<float *>(lds + E_P2);
-  const float cs = csum + __shfl_xor(csum, 32);
-  if (lane < 32) csh[qb][key] = cs;
-  if (qb == 1) {
+  // dv: lane's key kw, channels 16 cb + 4 (lane/16) .. +3
+  if (kok)
 #pragma unroll
-    for (int t = 0; t < TV; ++t)
+    for (int cb = 0; cb < NCV; ++cb)
+      *reinterpret_cast<f32x4 *>(dv_part + ((bos + j0 + kw) * HQ + hq) * DV + 16 * cb + 4 * gq) = dVa[cb];
+  float cs = csum + __shfl_xor(csum, 16);
+  cs += __shfl_xor(cs, 32);
+  if (gq == 0 && kok) cols_ds[(bos + j0 + kw) * HQ + hq] = cs;
+  // dk = ln2 2^(R_J - P2_j) dK, the chunk's running sums NCP channels at a time
+  __syncthreads();  // the LDS blocks are read
+  float *P2s = reinterpret_cast<float *>(Qb0);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Xv[key * XVS + 32 * t + crow(r, lane)] = dVa[t][r];
+  for (int c0 = 0; c0 < DK; c0 += NCP) {
+    part_p2<NCP>(g, off + ((cbase + J) * HQ + hq) * DK, bos + j0, nk, HQ, hq, DK, c0, P2s, tot);
+    if (kok)
 #pragma unroll
-    for (int t = 0; t < TK; ++t)
+      for (int cb = c0 / 16; cb < (c0 + NCP) / 16; ++cb) {
+        f32x4 o;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Xk[key * XKS + 32 * t + crow(r, lane)] = dKa[t][r];
+        for (int r = 0; r < 4; ++r) {
+          const int ch = 16 * cb + 4 * gq + r;
+          o[r] = LN2 * fast_exp2(Rj[ch] - P2s[kw * NCP + ch - c0]) * dKa[cb][r];
+        }
+        *reinterpret_cast<f32x4 *>(dk_part + ((bos + j0 + kw) * HQ + hq) * DK + 16 * cb + 4 * gq) = o;
+      }
+    __syncthreads();  // P2s is read before the next pass overwrites it
   }
-  __syncthreads();
-  if (qb == 0) {
-#pragma unroll
-    for (int t = 0; t < TV; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Xv[key * XVS + 32 * t + crow(r, lane)] += dVa[t][r];
-#pragma unroll
-    for (int t = 0; t < TK; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Xk[key * XKS + 32 * t + crow(r, lane)] += dKa[t][r];
-  }
-  __syncthreads();
-  for (int x = tid; x < nk * DV; x += 256) {
-    const int m = x / DV, c = x % DV;
-    dv_part[((bos + j0 + m) * HQ + hq) * DV + c] = Xv[m * XVS + c];
-  }
-  __syncthreads();  // dv is read out before P2s overwrites it
-  chunk_p2<DK>(g, off + ((cbase + J) * HQ + hq) * DK, bos + j0, nk, HQ, hq, P2s, tot);
-  for (int x = tid; x < nk * DK; x += 256) {
-    const int m = x / DK, c = x % DK;
-    dk_part[((bos + j0 + m) * HQ + hq) * DK + c] =
-        LN2 * fast_exp2(Rj[c] - P2s[m * DK + c]) * Xk[m * XKS + c];
-  }
-  if (tid < nk) cols_ds[(bos + j0 + tid) * HQ + hq] = csh[0][tid] + csh[1][tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -601,7 +717,7 @@ hipError_t bwd_mfma_t(const BwdProblem &b, const FwdWorkspace &ws, const BwdWork
   const int W = (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0);
   const dim3 grid((unsigned)(NCmax * p.HQ), (unsigned)p.nseg);
   const bool gs = p.g_scalar != nullptr;
-  auto kv = gs ? k_bwd_dkdv_mfma<DK, DV, true> : k_bwd_dkdv_mfma<DK, DV, false>;
+  auto kv = gs ? k_bwd_dkdv_w16<DK, DV, true> : k_bwd_dkdv_w16<DK, DV, false>;
   hipLaunchKernelGGL(kv, grid, dim3(256), 0, st, static_cast<const _Float16 *>(ws.kt),
                      static_cast<const _Float16 *>(bw.qbh), static_cast<const bf16_t *>(p.v),
                      static_cast<const bf16_t *>(b.dO), static_cast<const bf16_t *>(p.g), ws.csum,
