@@ -329,7 +329,7 @@ def main():
             "workload": c.name, "call": "wall_attn_bwd", "ms": round(ms_bwd, 3),
             "gflop": round(bflops / 1e9, 3), "TFLOP/s": round(btf, 2), "launches_timed": nb,
             # the whole call (pre-pass, both matrix-core kernels, running sums)
-            "roofline": {"kernel": "wall_attn_bwd (k_bwd_dkdv_mfma + k_bwd_dq_mfma + finishing)",
+            "roofline": {"kernel": "wall_attn_bwd (k_bwd_dkdv_w16 + k_bwd_dq_w16 + finishing)",
                          "bound": "mfma", "achieved": round(btf, 2), "peak": PEAK_MFMA_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(btf / PEAK_MFMA_TFLOPS, 4),
                          "traffic": None},

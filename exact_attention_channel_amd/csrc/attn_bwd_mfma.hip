@@ -29,13 +29,12 @@
 // rescaled q^T or k^T -- comes from row-major LDS tiles through
 // ds_read_b64_tr_b16, which hands lane i of each 16-lane group column i of
 // the 4 x 16 block its lanes address.  One workgroup per 64-key chunk walks
-// the query chunks that see it (dk, dv, column sums of ds: waves of 16 keys
-// on v_mfma_f32_16x16x32, the query blocks double-buffered in LDS through
-// LDS-direct loads); one per 64-row query chunk walks its key chunks (dq,
-// row sums: waves split a 64 x 64 block of pairs 2 x 2 on
-// v_mfma_f32_32x32x16, the next key chunk staged through registers).  The
-// float32 finishing kernels of attn_bwd.hip (reverse running sums, sums over
-// query heads) complete the gradients.
+// the query chunks that see it (dk, dv, column sums of ds); one per 64-row
+// query chunk walks its key chunks (dq, row sums).  Both use waves of 16
+// keys (16 rows) on v_mfma_f32_16x16x32, keep the wave's own rows in
+// registers, and double-buffer the walked blocks in LDS through LDS-direct
+// loads.  The float32 finishing kernels of attn_bwd.hip (reverse running
+// sums, sums over query heads) complete the gradients.
 #include <math.h>
 
 #include <type_traits>
@@ -49,53 +48,13 @@ namespace {
 constexpr int XC = CHUNK;  // 64 rows of a query chunk, keys of a key chunk
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-template <typename T> struct Mfma;
-template <> struct Mfma<_Float16> {
-  typedef f16x8 V;
-  static __device__ __forceinline__ f32x16 run(V a, V b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-  }
-};
-template <> struct Mfma<bf16_t> {
-  typedef bf16x8 V;
-  static __device__ __forceinline__ f32x16 run(V a, V b, f32x16 c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-  }
-};
-
-// Row of element r of a 32x32 MFMA result tile in lane `lane` (its column is lane % 32).
-__device__ __forceinline__ int crow(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
-
-// Operand (8 elements k = 8 (lane/32) .. +7 of row lane%32) of a row-major
-// LDS matrix [32 rows][stride] at column k0.
-template <typename T>
-__device__ __forceinline__ typename Mfma<T>::V row_operand(const T *M, int stride, int k0, int lane) {
-  return *reinterpret_cast<const typename Mfma<T>::V *>(M + (lane & 31) * stride + k0 + 8 * (lane >> 5));
-}
 
 __device__ __forceinline__ s16x4 tr16(const void *p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
-// A operand of a product that contracts over the rows x of a row-major LDS
-// matrix M [x][z] (stride in elements): output rows z0 .. z0+31, contraction
-// rows x0 + 4 (lane/32) + {0..3, 8..11} -- the rows a result tile's values
-// r = 0..7 hold (x0 = tile base + 16 m for its values 8m .. 8m+7).
-template <typename T>
-__device__ __forceinline__ typename Mfma<T>::V tr_operand(const T *M, int stride, int x0, int z0,
-                                                         int lane) {
-  const int row = x0 + 4 * (lane >> 5) + ((lane >> 2) & 3);
-  const int col = z0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const s16x4 lo = tr16(M + row * stride + col);
-  const s16x4 hi = tr16(M + (row + 8) * stride + col);
-  const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(typename Mfma<T>::V, v);
-}
-
-// B operand from a result tile's values 8m .. 8m+7, rounded to T.
+// B operand from 8 result values, rounded to half / bfloat16.
 __device__ __forceinline__ f16x8 pack_h(const float *x) {
   const u32x4 w = {pack_f16x2(x[0], x[1]), pack_f16x2(x[2], x[3]), pack_f16x2(x[4], x[5]),
                    pack_f16x2(x[6], x[7])};
@@ -107,56 +66,9 @@ __device__ __forceinline__ bf16x8 pack_b(const float *x) {
   return __builtin_bit_cast(bf16x8, w);
 }
 
-// Running decay sums (log2 units) of one chunk's rows into P2s [XC][DK].
-template <int DK>
-__device__ void chunk_p2(const bf16_t *__restrict__ g, const float *__restrict__ off_c, int64_t r0,
-                         int nrow, int HQ, int hq, float *P2s, float *tot) {
-  constexpr int NSEG = 256 / DK, RPS = XC / NSEG;
-  const int n = threadIdx.x % DK, sg = threadIdx.x / DK;
-  float x[RPS];  // the segment's rows, loaded together
-#pragma unroll
-  for (int i = 0; i < RPS; ++i) {
-    const int r = sg * RPS + i;
-    x[i] = r < nrow ? bf16_to_f32(g[((r0 + r) * HQ + hq) * DK + n]) : 0.f;
-  }
-  float acc = 0.f;
-#pragma unroll
-  for (int i = 0; i < RPS; ++i) {
-    acc += x[i];
-    P2s[(sg * RPS + i) * DK + n] = acc;
-  }
-  tot[sg * DK + n] = acc;
-  __syncthreads();
-  float base = off_c[n];
-  for (int q = 0; q < sg; ++q) base += tot[q * DK + n];
-  for (int r = sg * RPS; r < sg * RPS + RPS; ++r) P2s[r * DK + n] = (base + P2s[r * DK + n]) * LOG2E;
-  __syncthreads();
-}
-
 // 8 consecutive 16-bit elements (one 16-byte load); zeros past `valid`.
 __device__ __forceinline__ u32x4 ld16(const void *p, bool valid) {
   return valid ? *reinterpret_cast<const u32x4 *>(p) : u32x4{0u, 0u, 0u, 0u};
-}
-
-// 8 half values times 2^e[i] (e: integer-valued chunk factors, at most 4).
-__device__ __forceinline__ u32x4 rescale8(u32x4 w, const float *e) {
-  u32x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    o[i] = pack_f16x2(f16_lo(w[i]) * __builtin_amdgcn_ldexpf(1.f, (int)e[2 * i]),
-                      f16_hi(w[i]) * __builtin_amdgcn_ldexpf(1.f, (int)e[2 * i + 1]));
-  return o;
-}
-
-// Whether every chunk factor a[n] - b[n] of the DK channels is at most 4;
-// every wave decides it from its own lanes' share (channel lane + 64 c), so
-// all waves of a workgroup agree.
-template <int DK>
-__device__ __forceinline__ bool factors_in_range(const float *a, const float *b) {
-  float m = -INFINITY;
-#pragma unroll
-  for (int c = 0; c < DK / 64; ++c) m = fmaxf(m, a[c] - b[c]);
-  return wave_max(m) <= 4.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -509,31 +421,38 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_w16(
 }
 
 // ---------------------------------------------------------------------------
-// dq and the row sums of ds.  grid (NCmax*HQ, nseg): x = query chunk
-// (longest first) * HQ + head, y = segment.  Wave w: query rows 32 (w&1),
-// keys 32 (w>>1) of each 64 x 64 block; its q_hat and dO rows stay in
-// registers.
+// dq and the row sums of ds, with waves of 16 query rows.  grid
+// (NCmax*HQ, nseg): x = query chunk (longest first) * HQ + head, y = segment.
+// Wave w owns rows 16 w .. 16 w + 15 of the chunk against all 64 keys of
+// each key chunk, on v_mfma_f32_16x16x32:
+//   S^T[key, q]  = K''[key] . q_hat[q],   K'' = k_tilde 2^(A_I - R_J)
+//   dP^T[key, q] = v[key] . dO[q]
+//   dQ^T[ch, q] += K''^T ds^T
+// The wave's q_hat and dO rows stay in registers (B operands); a lane holds
+// one query row, whose lse, D and gate sum are scalars.  The key chunks' K''
+// and v and the keys' gate sums arrive by LDS-direct loads into two
+// buffers; each thread scales the k_tilde pieces it loaded by their
+// channels' factors (its anchors R_J loaded beside them).
 template <int DK, int DV, bool HAS_GS>
-__global__ __launch_bounds__(256, 2) void k_bwd_dq_mfma(
+__global__ __launch_bounds__(256, 2) void k_bwd_dq_w16(
     const _Float16 *__restrict__ kt, const _Float16 *__restrict__ qbh, const bf16_t *__restrict__ v,
     const bf16_t *__restrict__ dO, const bf16_t *__restrict__ g, const float *__restrict__ off,
     const float *__restrict__ anch, const float *__restrict__ gsum, const float *__restrict__ lse,
     const float *__restrict__ Dv, int *__restrict__ wide, float *__restrict__ dq32,
     float *__restrict__ rows_ds, const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ,
     int H, int NCmax, int window, float scale) {
-  constexpr int KS = DK + 8, VS = DV + 8;
-  constexpr int KX = DK + 16;
-  constexpr int TK = DK / 32;
-  constexpr int QI = XC * DK / 8 / 256, OI = XC * DV / 8 / 256;
-  constexpr int O_KT = 0, O_VS = O_KT + XC * KS * 2, O_LOOP = O_VS + XC * VS * 2;
-  constexpr int XQS = DK + 1;
-  constexpr int E_P2 = XC * XQS * 4, E_END = E_P2 + XC * DK * 4;
-  constexpr int LDS_BYTES = O_LOOP > E_END ? O_LOOP : E_END;
-  __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
-  __shared__ __attribute__((aligned(16))) float Aq[DK], Gj[XC], rsh[2][XC];
+  constexpr int KX = DK + 16;                       // k_tilde row in the forward workspace
+  constexpr int KB = XC * DK * 2, VB = XC * DV * 2;  // bytes of a key / value chunk
+  constexpr int NKD = KB / 1024, NVD = VB / 1024;    // 1-KiB LDS-direct loads per chunk
+  constexpr int NSK = DK / 32, NSV = DV / 32;        // 32-channel steps of S^T and dP^T
+  constexpr int NCK = DK / 16;                       // 16-channel blocks of dQ^T
+  constexpr int NCP = KB / (XC * 4) < 64 ? KB / (XC * 4) : 64;  // channels per epilogue pass
+  static_assert(NKD % 4 == 0 && NVD % 4 == 0, "a chunk is a multiple of 4 KiB");
+  __shared__ __attribute__((aligned(16))) unsigned char Kb0[KB], Kb1[KB];
+  __shared__ __attribute__((aligned(16))) unsigned char Vb0[VB], Vb1[VB];
+  __shared__ __attribute__((aligned(16))) float Gb0[XC], Gb1[XC];
+  __shared__ __attribute__((aligned(16))) float Aq[DK];
   __shared__ float tot[256];
-  _Float16 *Kt = reinterpret_cast<_Float16 *>(lds + O_KT);
-  bf16_t *Vs = reinterpret_cast<bf16_t *>(lds + O_VS);
 
   const int hq = blockIdx.x % HQ, seg = blockIdx.y;
   if (__builtin_amdgcn_readfirstlane(wide[seg * HQ + hq]) != 0) return;
@@ -545,114 +464,132 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_mfma(
   if (I >= nch) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = w & 1, kb = w >> 1;
+  const int c16 = lane & 15, gq = lane >> 4;
   const int h = hq / (HQ / H);
   const int i0 = I * XC, nq = min(XC, L - i0);
   const int64_t cbase = (int64_t)seg * NCmax;
-  const float *anch_h = anch + (int64_t)hq * DK;
+  const int qw = 16 * w + c16;  // this lane's query row in the chunk
+  const bool qok = qw < nq;
+  const int64_t tq = bos + i0 + qw;
 
-  // this lane's query row: q_hat and dO as B operands, row statistics
-  const int qrow = 32 * qb + (lane & 31);
-  const bool qok = qrow < nq;
-  const int64_t tq = bos + i0 + qrow;
-  f16x8 qreg[DK / 16];
-  bf16x8 oreg[DV / 16];
+  // the wave's rows as B operands (channels 32 s + 8 (lane/16) ..), the lane's row statistics
+  f16x8 qr[NSK];
+  bf16x8 orr[NSV];
 #pragma unroll
-  for (int ks = 0; ks < DK / 16; ++ks)
-    qreg[ks] = __builtin_bit_cast(
-        f16x8, ld16(qbh + ((int64_t)hq * ntok + tq) * DK + 16 * ks + 8 * (lane >> 5), qok));
+  for (int s = 0; s < NSK; ++s)
+    qr[s] = __builtin_bit_cast(f16x8, ld16(qbh + ((int64_t)hq * ntok + tq) * DK + 32 * s + 8 * gq, qok));
 #pragma unroll
-  for (int ks = 0; ks < DV / 16; ++ks)
-    oreg[ks] = __builtin_bit_cast(bf16x8, ld16(dO + (tq * HQ + hq) * DV + 16 * ks + 8 * (lane >> 5), qok));
+  for (int s = 0; s < NSV; ++s)
+    orr[s] = __builtin_bit_cast(bf16x8, ld16(dO + (tq * HQ + hq) * DV + 32 * s + 8 * gq, qok));
   const float Lr = qok ? lse[tq * HQ + hq] * LOG2E : 0.f;
   const float Dr = qok ? Dv[tq * HQ + hq] : 0.f;
   const float Gr = (HAS_GS && qok) ? gsum[tq * HQ + hq] : 0.f;
-  if (tid < DK) Aq[tid] = anch_h[(cbase + I) * HQ * DK + tid];
-  __syncthreads();
+  if (tid < DK) Aq[tid] = anch[((cbase + I) * HQ + hq) * DK + tid];
+  __syncthreads();  // Aq is read by every wave
 
-  const int pk = tid % (DK / 8), pv = tid % (DV / 8);
-  float aqw[DK / 64];
+  // sources of the key chunks (rows relative to bos; rows past L read zero)
+  const __amdgpu_buffer_rsrc_t k_rs =
+      make_rsrc(kt + uniform64(((int64_t)hq * ntok + bos) * KX), uniform64(((int64_t)(L - 1) * KX + DK) * 2));
+  const __amdgpu_buffer_rsrc_t v_rs =
+      make_rsrc(v + uniform64((bos * H + h) * DV), uniform64(((int64_t)(L - 1) * H * DV + DV) * 2));
+  const __amdgpu_buffer_rsrc_t g_rs =
+      make_rsrc(gsum + uniform64(bos * HQ + hq), uniform64(HAS_GS ? ((int64_t)(L - 1) * HQ + 1) * 4 : 0));
+  // key chunk J into a buffer: load m of a tile by wave m % 4, lane l filling
+  // LDS piece 64 m + l (row r, piece pp) from piece pp ^ qswz(r) of row r
+  auto issue = [&](int J, unsigned char *Kb, unsigned char *Vb, float *Gb) {
+    const int j0 = J * XC;
 #pragma unroll
-  for (int c = 0; c < DK / 64; ++c) aqw[c] = Aq[lane + 64 * c];
-
-  u32x4 fk[QI], fv[OI];
-  float fe8[8], frw[DK / 64], fg = 0.f;
-  auto fetch = [&](int J) {
-    const int j0 = J * XC, nk = min(XC, L - j0);
-#pragma unroll
-    for (int u = 0; u < QI; ++u) {
-      const int r = (tid + 256 * u) / (DK / 8);
-      fk[u] = ld16(kt + ((int64_t)hq * ntok + bos + j0 + r) * KX + 8 * pk, r < nk);
+    for (int mm = 0; mm < NKD / 4; ++mm) {
+      const int m = w + 4 * mm, gi = 64 * m + lane, r = gi / (DK / 8), pp = gi % (DK / 8);
+      dma16(k_rs, Kb + 1024 * m, ((j0 + r) * KX + 8 * (pp ^ qswz<DK>(r))) * 2);
     }
 #pragma unroll
-    for (int u = 0; u < OI; ++u) {
-      const int r = (tid + 256 * u) / (DV / 8);
-      fv[u] = ld16(v + ((bos + j0 + r) * H + h) * DV + 8 * pv, r < nk);
+    for (int mm = 0; mm < NVD / 4; ++mm) {
+      const int m = w + 4 * mm, gi = 64 * m + lane, r = gi / (DV / 8), pp = gi % (DV / 8);
+      dma16(v_rs, Vb + 1024 * m, ((j0 + r) * H * DV + 8 * (pp ^ qswz<DV>(r))) * 2);
     }
-    const float *rJ = anch_h + (cbase + J) * HQ * DK;
-    const f32x4 a0 = *reinterpret_cast<const f32x4 *>(rJ + 8 * pk);
-    const f32x4 a1 = *reinterpret_cast<const f32x4 *>(rJ + 8 * pk + 4);
+    if (HAS_GS && w == 0) dma4(g_rs, Gb, (j0 + lane) * HQ * 4);
+  };
+  // This thread's k_tilde pieces share one 8-channel group (their rows agree
+  // mod 16); the chunk's anchors for it and for the range check load with
+  // each chunk.
+  const int lpk = (lane % (DK / 8)) ^ qswz<DK>((64 * w + lane) / (DK / 8));
+  f32x4 ar0, ar1;
+  float arc[DK / 64];
+  auto load_anchors = [&](int J) {
+    const float *aJ = anch + ((cbase + J) * HQ + hq) * DK;
+    ar0 = *reinterpret_cast<const f32x4 *>(aJ + 8 * lpk);
+    ar1 = *reinterpret_cast<const f32x4 *>(aJ + 8 * lpk + 4);
+#pragma unroll
+    for (int c = 0; c < DK / 64; ++c) arc[c] = aJ[lane + 64 * c];
+  };
+  auto scale_own = [&](unsigned char *Kb) -> bool {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < DK / 64; ++c) mx = fmaxf(mx, Aq[lane + 64 * c] - arc[c]);
+    if (wave_max(mx) > 4.f) return false;
+    const f32x4 q0 = *reinterpret_cast<const f32x4 *>(Aq + 8 * lpk);
+    const f32x4 q1 = *reinterpret_cast<const f32x4 *>(Aq + 8 * lpk + 4);
+    f16x8 fac;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      fe8[e] = Aq[8 * pk + e] - a0[e];
-      fe8[4 + e] = Aq[8 * pk + 4 + e] - a1[e];
+      fac[e] = (_Float16)__builtin_amdgcn_ldexpf(1.f, (int)(q0[e] - ar0[e]));
+      fac[4 + e] = (_Float16)__builtin_amdgcn_ldexpf(1.f, (int)(q1[e] - ar1[e]));
     }
 #pragma unroll
-    for (int c = 0; c < DK / 64; ++c) frw[c] = rJ[lane + 64 * c];
-    if (tid < XC) fg = (HAS_GS && tid < nk) ? gsum[(bos + j0 + tid) * HQ + hq] : 0.f;
-  };
-  // registers -> LDS: K'' = k_tilde 2^(A_I - R_J), v, gate sums; false
-  // (nothing written) when a chunk factor is out of range
-  auto commit = [&]() {
-    if (!factors_in_range<DK>(aqw, frw)) return false;
-#pragma unroll
-    for (int u = 0; u < QI; ++u) {
-      const int r = (tid + 256 * u) / (DK / 8);
-      *reinterpret_cast<u32x4 *>(Kt + r * KS + 8 * pk) = rescale8(fk[u], fe8);
+    for (int mm = 0; mm < NKD / 4; ++mm) {
+      f16x8 *pc = reinterpret_cast<f16x8 *>(Kb + 1024 * (w + 4 * mm) + 16 * lane);
+      *pc = *pc * fac;
     }
-#pragma unroll
-    for (int u = 0; u < OI; ++u) {
-      const int r = (tid + 256 * u) / (DV / 8);
-      *reinterpret_cast<u32x4 *>(Vs + r * VS + 8 * pv) = fv[u];
-    }
-    if (tid < XC) Gj[tid] = fg;
     return true;
   };
 
-  f32x16 dQa[TK];
+  f32x4 dQa[NCK];
 #pragma unroll
-  for (int t = 0; t < TK; ++t) dQa[t] = f32x16{};
+  for (int t = 0; t < NCK; ++t) dQa[t] = f32x4{};
   float rsum = 0.f;
-
   const int Jlo = window > 0 ? max(0, i0 - window + 1) / XC : 0;
-  const int irel = i0 + qrow;
-  fetch(Jlo);
-  if (!commit()) {
-    if (tid == 0) wide[seg * HQ + hq] = 1;
-    return;
-  }
-  __syncthreads();
-  for (int J = Jlo; J <= I; ++J) {
+  const int irel = i0 + qw;
+
+  auto block = [&](auto par_c, int J) {
+    constexpr int P = decltype(par_c)::value;
+    const unsigned char *const Kb = P ? Kb1 : Kb0;
+    const unsigned char *const Vb = P ? Vb1 : Vb0;
+    const float *const Gb = P ? Gb1 : Gb0;
+    if (J < I) {
+      issue(J + 1, P ? Kb0 : Kb1, P ? Vb0 : Vb1, P ? Gb0 : Gb1);
+      load_anchors(J + 1);
+    }
+    const _Float16 *Kh = reinterpret_cast<const _Float16 *>(Kb);
+    const bf16_t *Vh = reinterpret_cast<const bf16_t *>(Vb);
+    // S^T = K'' q_hat^T and dP^T = v dO^T: four 16-key tiles
+    f32x4 S[4], dPt[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) S[t] = dPt[t] = f32x4{};
+#pragma unroll
+    for (int s = 0; s < NSK; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        S[t] = Mfma16<_Float16>::run(
+            *reinterpret_cast<const f16x8 *>(Kh + qpiece<DK>(16 * t + c16, 4 * s + gq)), qr[s], S[t]);
+#pragma unroll
+    for (int s = 0; s < NSV; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        dPt[t] = Mfma16<bf16_t>::run(
+            *reinterpret_cast<const bf16x8 *>(Vh + qpiece<DV>(16 * t + c16, 4 * s + gq)), orr[s], dPt[t]);
+    // ds: lane's row qw, keys 16 t + 4 (lane/16) + e
     const int j0 = J * XC, nk = min(XC, L - j0);
-    // S^T = K'' Q^T, dP^T = V dO^T for keys 32 kb, rows 32 qb
-    f32x16 S = f32x16{}, dP = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < DK / 16; ++ks)
-      S = Mfma<_Float16>::run(row_operand(Kt + 32 * kb * KS, KS, 16 * ks, lane), qreg[ks], S);
-#pragma unroll
-    for (int ks = 0; ks < DV / 16; ++ks)
-      dP = Mfma<bf16_t>::run(row_operand(Vs + 32 * kb * VS, VS, 16 * ks, lane), oreg[ks], dP);
     const bool full = nq == XC && nk == XC && I > J && !(window > 0 && i0 + XC - 1 - j0 >= window);
     float dsv[16];
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int m0 = 32 * kb + 8 * a + 4 * (lane >> 5);  // keys m0 .. m0+3 (values 4a .. 4a+3)
+    for (int t = 0; t < 4; ++t) {
+      const int m0 = 16 * t + 4 * gq;
       f32x4 g4 = f32x4{};
-      if (HAS_GS) g4 = *reinterpret_cast<const f32x4 *>(Gj + m0);
+      if (HAS_GS) g4 = *reinterpret_cast<const f32x4 *>(Gb + m0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 4 * a + e;
-        float s2 = S[r];
+        float s2 = S[t][e];
         if (HAS_GS) s2 += Gr - g4[e];
         bool ok = true;
         if (!full) {
@@ -660,53 +597,68 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dq_mfma(
           ok = qok && m0 + e < nk && jrel <= irel && !(window > 0 && irel - jrel >= window);
         }
         const float p = ok ? fast_exp2(s2 - Lr) : 0.f;
-        const float ds = p * (dP[r] - Dr);
-        dsv[r] = ds;
+        const float ds = p * (dPt[t][e] - Dr);
+        dsv[4 * t + e] = ds;
         rsum += ds;
       }
     }
-    // dQ^T += K''^T ds^T, contracting over the 32 keys
+    // dQ^T += K''^T ds^T over two 32-key steps
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const f16x8 db = pack_h(dsv + 8 * m);
+    for (int u = 0; u < 2; ++u) {
+      const f16x8 db = pack_h(dsv + 8 * u);
 #pragma unroll
-      for (int t = 0; t < TK; ++t)
-        dQa[t] = Mfma<_Float16>::run(tr_operand(Kt, KS, 32 * kb + 16 * m, 32 * t, lane), db, dQa[t]);
+      for (int cb = 0; cb < NCK; ++cb)
+        dQa[cb] = Mfma16<_Float16>::run(tr16_operand<_Float16, DK>(Kh, 32 * u, 16 * cb, lane), db, dQa[cb]);
     }
+  };
+
+  issue(Jlo, Kb0, Vb0, Gb0);
+  load_anchors(Jlo);
+  vm_wait0();
+  bool in_range = scale_own(Kb0);
+  __syncthreads();
+  for (int J = Jlo; in_range;) {
+    block(std::integral_constant<int, 0>{}, J);
+    if (J == I) break;
+    ++J;
+    vm_wait0();
+    in_range = scale_own(Kb1);
     __syncthreads();
-    if (J < I) {
-      fetch(J + 1);
-      if (!commit()) {
-        if (tid == 0) wide[seg * HQ + hq] = 1;
-        return;
-      }
-      __syncthreads();
-    }
+    if (!in_range) break;
+    block(std::integral_constant<int, 1>{}, J);
+    if (J == I) break;
+    ++J;
+    vm_wait0();
+    in_range = scale_own(Kb0);
+    __syncthreads();
+  }
+  if (!in_range) {  // a chunk factor above 2^4: the float32 kernels take the pair
+    if (tid == 0) wide[seg * HQ + hq] = 1;
+    return;
   }
 
-  float *Xq = reinterpret_cast<float *>(lds);
-  float *P2s = reinterpret_cast<float *>(lds + E_P2);
-  const float rs = rsum + __shfl_xor(rsum, 32);
-  if (lane < 32) rsh[kb][qrow] = rs;
-  if (kb == 1) {
+  float rs = rsum + __shfl_xor(rsum, 16);
+  rs += __shfl_xor(rs, 32);
+  if (gq == 0 && qok) rows_ds[tq * HQ + hq] = rs;
+  // dq = scale 2^(P2_i - A_I) dQ, the chunk's running sums NCP channels at a time
+  __syncthreads();  // the LDS chunks are read
+  float *P2s = reinterpret_cast<float *>(Kb0);
 #pragma unroll
-    for (int t = 0; t < TK; ++t)
+  for (int c0 = 0; c0 < DK; c0 += NCP) {
+    part_p2<NCP>(g, off + ((cbase + I) * HQ + hq) * DK, bos + i0, nq, HQ, hq, DK, c0, P2s, tot);
+    if (qok)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Xq[qrow * XQS + 32 * t + crow(r, lane)] = dQa[t][r];
+      for (int cb = c0 / 16; cb < (c0 + NCP) / 16; ++cb) {
+        f32x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int ch = 16 * cb + 4 * gq + r;
+          o[r] = scale * fast_exp2(P2s[qw * NCP + ch - c0] - Aq[ch]) * dQa[cb][r];
+        }
+        *reinterpret_cast<f32x4 *>(dq32 + (tq * HQ + hq) * DK + 16 * cb + 4 * gq) = o;
+      }
+    __syncthreads();  // P2s is read before the next pass overwrites it
   }
-  __syncthreads();
-  if (kb == 0) {
-#pragma unroll
-    for (int t = 0; t < TK; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Xq[qrow * XQS + 32 * t + crow(r, lane)] += dQa[t][r];
-  }
-  chunk_p2<DK>(g, off + ((cbase + I) * HQ + hq) * DK, bos + i0, nq, HQ, hq, P2s, tot);
-  for (int x = tid; x < nq * DK; x += 256) {
-    const int m = x / DK, c = x % DK;
-    dq32[((bos + i0 + m) * HQ + hq) * DK + c] = scale * fast_exp2(P2s[m * DK + c] - Aq[c]) * Xq[m * XQS + c];
-  }
-  if (tid < nq) rows_ds[(bos + i0 + tid) * HQ + hq] = rsh[0][tid] + rsh[1][tid];
 }
 
 template <int DK, int DV>
@@ -723,7 +675,7 @@ hipError_t bwd_mfma_t(const BwdProblem &b, const FwdWorkspace &ws, const BwdWork
                      static_cast<const bf16_t *>(b.dO), static_cast<const bf16_t *>(p.g), ws.csum,
                      ws.anch, ws.gsum, b.lse, bw.Dv, ws.wide, bw.dk_part, bw.dv_part, bw.cols_ds,
                      p.cu, p.T, p.ntok, (int)p.HQ, (int)p.H, NCmax, W);
-  auto qk = gs ? k_bwd_dq_mfma<DK, DV, true> : k_bwd_dq_mfma<DK, DV, false>;
+  auto qk = gs ? k_bwd_dq_w16<DK, DV, true> : k_bwd_dq_w16<DK, DV, false>;
   hipLaunchKernelGGL(qk, grid, dim3(256), 0, st, static_cast<const _Float16 *>(ws.kt),
                      static_cast<const _Float16 *>(bw.qbh), static_cast<const bf16_t *>(p.v),
                      static_cast<const bf16_t *>(b.dO), static_cast<const bf16_t *>(p.g), ws.csum,
