@@ -100,6 +100,23 @@ def test_backward_matches_oracle(wa, c):
     check_grads(got, ref, TOL[c.dtype], c.name)
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_backward_varlen_with_empty_sequences(wa, dtype):
+    """cu_seqlens with zero-length sequences first, in the middle and in a
+    row, next to sequences of one to three 64-token chunks."""
+    c = cfg("bwd_varlen_empty", 1, 0, 4, 2, 64, 64, dtype, nseq=9, len_lo=0, len_hi=90, window=33,
+            g_scalar_std=0.01, sink=True, seed=41)
+    x = W.make_prefill(c)
+    assert x["q"].shape[1] == 350
+    x["cu_seqlens"] = torch.tensor([0, 0, 13, 13, 13, 124, 141, 141, 292, 350], dtype=torch.int32)
+    dO = torch.randn(x["q"].shape[:3] + (c.V,), generator=torch.Generator().manual_seed(1041)).to(dtype)
+    got = grads_gpu(wa, x, dO)
+    ref = oracle.wall_attn_bwd(x["q"], x["k"], x["v"], x["g"], dO, scale=x["scale"],
+                               g_scalar=x["g_scalar"], sink_bias=x["sink_bias"],
+                               window_size=x["window_size"], cu_seqlens=x["cu_seqlens"])
+    check_grads(got, ref, TOL[dtype], "backward, varlen with empty sequences")
+
+
 def test_backward_deterministic(wa):
     c = CASES[1]
     x = W.make_prefill(c)
