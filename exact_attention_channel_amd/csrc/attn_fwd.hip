@@ -145,6 +145,23 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *
 }
 __device__ __forceinline__ void vm_wait0() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0) only
 
+// Sum of the eight bfloat16 probabilities of a value-product operand, added
+// to acc: four v_dot2c_f32_bf16 against (1, 1).  The row sum is thus taken
+// over the same rounded probabilities that meet the values.  The empty asm
+// ties the result to this point of the instruction stream, so the compiler
+// cannot sink the additions past the matrix-core block they are issued in.
+__device__ __forceinline__ float bf16x8_sum(const bf16x8 &p, float acc) {
+  const bf16x2 one = __builtin_bit_cast(bf16x2, 0x3f803f80u);
+  // (pairs taken with constant shuffles: a bit cast of the vector's 32-bit
+  // words to bfloat16 pairs compiled to the first word four times)
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
+  __asm__ volatile("" : "+v"(acc));
+  return acc;
+}
+
 template <int DK, int DV, bool HAS_GS>
 __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     const bf16_t *__restrict__ q, const bf16_t *__restrict__ k, const bf16_t *__restrict__ g,
@@ -271,9 +288,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     float qmx = 0.f;
     const int cw = qw0 / CHUNK, r0 = cw * CHUNK;  // the rows' chunk and its first row
     const bool second = qw0 > r0;                 // the wave's rows are the chunk's second half
+    // acc: the exponent of q_hat's factor in log2 units, with log2(qscale)
+    // folded in, so that each row costs one fma, one exp2 and one multiply
+    // per channel: acc = P2 - RQ_I + log2(qscale), P2 = (offset + g sum) log2(e)
+    const float lq = __builtin_amdgcn_logf(qscale);
     float acc[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = off[((cbase + cw) * HQ + hq) * DK + CPL * lane + c];
+    for (int c = 0; c < CPL; ++c) acc[c] = off[((cbase + cw) * HQ + hq) * DK + CPL * lane + c] * LOG2E - rq[c] + lq;
     // buffer loads: the row offset is a scalar, and rows past the sequence
     // read as zero without a branch per row
     const int64_t ext = ((int64_t)(L - 1) * qrow + DK) * 2;
@@ -293,22 +314,22 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     }
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
-      acc[0] += bf16_lo(gp[u]);
-      if (CPL == 2) acc[CPL - 1] += bf16_hi(gp[u]);
+      acc[0] = fmaf(bf16_lo(gp[u]), LOG2E, acc[0]);
+      if (CPL == 2) acc[CPL - 1] = fmaf(bf16_hi(gp[u]), LOG2E, acc[CPL - 1]);
     }
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
       float qv[CPL];
-      acc[0] += bf16_lo(gw[u]);
+      acc[0] = fmaf(bf16_lo(gw[u]), LOG2E, acc[0]);
       qv[0] = bf16_lo(qw[u]);
       if (CPL == 2) {
-        acc[CPL - 1] += bf16_hi(gw[u]);
+        acc[CPL - 1] = fmaf(bf16_hi(gw[u]), LOG2E, acc[CPL - 1]);
         qv[CPL - 1] = bf16_hi(qw[u]);
       }
       float qo[CPL];
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
-        qo[c] = qv[c] * fast_exp2(acc[c] * LOG2E - rq[c]) * qscale;
+        qo[c] = qv[c] * fast_exp2(acc[c]);
         qmx = fmaxf(qmx, fabsf(qo[c]));
       }
       unsigned char *dst = &Qs[(wv * 32 + u) * QSB + 2 * CPL * lane];
@@ -322,16 +343,17 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     (void)frexpf(qmx, &ex);  // qmx < 2^ex
     qexp = __builtin_amdgcn_readfirstlane(max(ex, -8));
   };
-  auto load_a = [&](int chunk) {  // anchors of a key chunk, this lane's channels
+  auto load_anch = [&](int chunk, float (&a)[CPL]) {  // anchors of a key chunk, this lane's channels
     const int soff = chunk * HQ * DK * 4;
     if (CPL == 2) {
       const u32x2 x = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(an_rs, lane * 8, soff, 0));
-      araw[0] = __uint_as_float(x[0]);
-      araw[CPL - 1] = __uint_as_float(x[1]);
+      a[0] = __uint_as_float(x[0]);
+      a[CPL - 1] = __uint_as_float(x[1]);
     } else {
-      araw[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(an_rs, lane * 4, soff, 0));
+      a[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(an_rs, lane * 4, soff, 0));
     }
   };
+  auto load_a = [&](int chunk) { load_anch(chunk, araw); };
 
   // ---- query operand ----
   f16x8 qB[NKS];
@@ -523,17 +545,13 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   bool m_set = false, all_set = false, ovf = false;
   float m_true = -INFINITY;
   auto tail = [&](f32x16 &S, bf16x8 (&pB)[2]) {
-    float rs = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = fast_exp2(S[r]);
-      S[r] = p;
-      rs += p;
-    }
-    l_part += rs;
-    ovf = ovf || !(rs <= PBIG);
+    for (int r = 0; r < 16; ++r) S[r] = fast_exp2(S[r]);
     pB[0] = __builtin_convertvector(__builtin_shufflevector(S, S, 0, 1, 2, 3, 4, 5, 6, 7), bf16x8);
     pB[1] = __builtin_convertvector(__builtin_shufflevector(S, S, 8, 9, 10, 11, 12, 13, 14, 15), bf16x8);
+    const float rs = bf16x8_sum(pB[1], bf16x8_sum(pB[0], 0.f));
+    l_part += rs;
+    ovf = ovf || !(rs <= PBIG);
   };
   // rows without a reference yet take this tile's max (nothing is
   // accumulated for them, so nothing needs rescaling)
@@ -585,7 +603,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     if (VR >= 0 && wv + NWV * VR < BT::NVI) dma16(v_rs, vbuf + 1024 * (wv + NWV * VR), voff[VR], Jv * BK * vrow * 2);
     float pr[16];
     bf16x8 pb[2];
-    float rs[2] = {0.f, 0.f};
+    float rs = 0.f;
 #pragma unroll
     for (int i = 0; i < NKS; ++i) {
       if (FO.slot_s[i] < KAHEAD) kread(i);
@@ -624,7 +642,6 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
         for (int e = 0; e < E; ++e) {
           if (e < e0 || e >= e1) continue;
           pr[e] = fast_exp2(Sc[e]);
-          rs[e & 1] += pr[e];
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st)
@@ -633,11 +650,11 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
 #pragma unroll
             for (int r = 0; r < 8; ++r) p8[r] = pr[8 * st + r];
             pb[st] = __builtin_convertvector(p8, bf16x8);
+            rs = bf16x8_sum(pb[st], rs);
           }
         if (e1 == E) {
-          const float t = rs[0] + rs[1];
-          l_part += t;
-          ovf = ovf || !(t <= PBIG);
+          l_part += rs;
+          ovf = ovf || !(rs <= PBIG);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -675,21 +692,30 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     auto chunkOf = [&](int t) { return tileJ(t) >> 1; };  // tile indices are never negative
     auto new_chunk = [&](int t) { return t == 0 || chunkOf(t) != chunkOf(t - 1); };
     if (MODE != 0) __syncthreads();  // the previous sweep's reads of the tile buffers are done
+    // the anchors of the first three tiles' chunks load together, ahead of
+    // the tile loads and q_hat
+    const bool nc1 = 1 < NTL && new_chunk(1);
+    const bool nc2p = 2 < NTL && new_chunk(2);
+    float a1[CPL], a2[CPL];
     load_a(chunkOf(0));
+    if (nc1) load_anch(chunkOf(1), a1);
+    if (nc2p) load_anch(chunkOf(2), a2);
     dma_k(tileJ(0), K0);
     if (VAL) dma_v(tileJ(0), V0);
     if (1 < NTL) dma_k(tileJ(1), K1);
     if (MODE == 0) make_qhat();  // overlaps the first tile loads
     float cs_cur = factors();
     rebuild();
-    const bool nc1 = 1 < NTL && new_chunk(1);
     float cs_next = cs_cur;
     if (nc1) {
-      load_a(chunkOf(1));
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) araw[c] = a1[c];
       cs_next = factors();
     }
-    const bool nc2p = 2 < NTL && new_chunk(2);
-    if (nc2p) load_a(chunkOf(2));
+    if (nc2p) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) araw[c] = a2[c];
+    }
     vm_wait0();
     __syncthreads();
     f32x16 Sa, Sb;

@@ -348,8 +348,18 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   const int64_t cidx = (int64_t)s * NCmax + c;
   const FV<CPT> base = loadv<float, CPT>(off + (cidx * HQ + hq) * KD + CPT * cgi);
   const FV<CPT> A = loadv<float, CPT>(anch + (cidx * HQ + hq) * KD + CPT * cgi);
+  // anchor of the query tile (its first chunk): q_hat = q 2^(P2 - RQ)
+  const int64_t cq = (int64_t)s * NCmax + (c & ~1);
+  const FV<CPT> RQ = loadv<float, CPT>(anch + (cq * HQ + hq) * KD + CPT * cgi);
+  // the gate's chunk offset and this row's g_scalar (first wave)
+  float gs_x = 0.f, gs_off = 0.f;
+  if (gs != nullptr && threadIdx.x < 64) {
+    gs_x = (int)threadIdx.x < nrow ? Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.f;
+    gs_off = off_s[cidx * HQ + hq];
+  }
   // the rows' keys (and queries, where this pass rescales them) load
-  // together with g, ahead of the in-chunk scan: one memory round trip
+  // together with g, ahead of the in-chunk scan: every load of the
+  // workgroup goes out in one memory round trip
   constexpr bool QL = !HM || QBH;  // queries needed below
   u32x4 kin[CS::RPG], qin[CS::RPG];
 #pragma unroll
@@ -362,9 +372,6 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   }
   FV<CPT> p2[CS::RPG];
   CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
-  // anchor of the query tile (its first chunk): q_hat = q 2^(P2 - RQ)
-  const int64_t cq = (int64_t)s * NCmax + (c & ~1);
-  const FV<CPT> RQ = loadv<float, CPT>(anch + (cq * HQ + hq) * KD + CPT * cgi);
   // Range of the anchored operands: the exponents of q_hat and k_tilde stay
   // within EMAX (and the half keys and gate sums below their limits), else
   // the (segment, head) goes to the exact path.  The benchmark workloads
@@ -417,9 +424,8 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
     const int r = threadIdx.x;
     float G = 0.f;
     if (gs != nullptr) {
-      float x = r < nrow ? Elem<TE>::ld(gs + (r0 + r) * HQ + hq) : 0.f;
-      x = wave_inclusive_scan(x);
-      G = (off_s[cidx * HQ + hq] + x) * LOG2E;
+      const float x = wave_inclusive_scan(gs_x);
+      G = (gs_off + x) * LOG2E;
       if (r < nrow) gsum[(r0 + r) * HQ + hq] = G;
       // the half keys carry -G split into two halves
       if (HM && r < nrow && !(fabsf(G) < 16384.f)) wide[s * HQ + hq] = 1;
