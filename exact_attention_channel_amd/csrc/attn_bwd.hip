@@ -302,39 +302,123 @@ __global__ __launch_bounds__(256) void k_bwd_dkdv(
   }
 }
 
+// Four consecutive channels of a row as floats (8 bytes of bfloat16 or 16
+// of float), and back in the input type (round to nearest even).
+template <typename TE> __device__ __forceinline__ f32x4 ld4(const TE *p);
+template <> __device__ __forceinline__ f32x4 ld4<bf16_t>(const bf16_t *p) {
+  const u32x2 w = *reinterpret_cast<const u32x2 *>(p);
+  return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+}
+template <> __device__ __forceinline__ f32x4 ld4<float>(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+__device__ __forceinline__ f32x4 ld4f(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+template <typename TE> __device__ __forceinline__ void st4(TE *p, f32x4 x);
+template <> __device__ __forceinline__ void st4<bf16_t>(bf16_t *p, f32x4 x) {
+  *reinterpret_cast<u32x2 *>(p) = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+}
+template <> __device__ __forceinline__ void st4<float>(float *p, f32x4 x) { *reinterpret_cast<f32x4 *>(p) = x; }
+
+// Row stride of the chunk totals: DK channel totals, the dGs total at DK,
+// padding to a multiple of four floats (16-byte loads of any four channels).
+template <int DK> constexpr int ctot_stride() { return DK + 4; }
+
+// Thread layout of the two kernels below: a thread owns channels 4 cg ..
+// 4 cg + 3 of RPG consecutive rows of the 64-row chunk, grp * RPG .. + RPG-1.
+template <int DK> struct ChunkRows {
+  static constexpr int NQ = DK / 4, NG = 256 / NQ, RPG = XC / NG;
+};
+
+// The same four channels kept raw (loaded early, converted where used).
+template <typename TE> struct Raw4;
+template <> struct Raw4<bf16_t> {
+  typedef u32x2 T;
+  static __device__ __forceinline__ T ld(const bf16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
+  static __device__ __forceinline__ f32x4 cvt(T w) { return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])}; }
+};
+template <> struct Raw4<float> {
+  typedef f32x4 T;
+  static __device__ __forceinline__ T ld(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+  static __device__ __forceinline__ f32x4 cvt(T w) { return w; }
+};
+
+// dP_tn = q_tn dq_tn - k_tn dk(hq)_tn for the thread's rows (zero past the
+// sequence), and the rows' dq.  Rows past the sequence load its last row
+// (L > r0: the chunk holds at least one row), so that every load is
+// unconditional and all of them go out before the first use.
+template <typename TE, int DK>
+__device__ __forceinline__ void chunk_dp(const TE *q, const TE *k, const float *dq32, const float *dk_part,
+                                         int64_t bos, int r0, int L, int HQ, int H, int hq, f32x4 (&x)[ChunkRows<DK>::RPG],
+                                         f32x4 (&dqv)[ChunkRows<DK>::RPG]) {
+  typedef ChunkRows<DK> CR;
+  typedef Raw4<TE> R;
+  const int cg = threadIdx.x % CR::NQ, grp = threadIdx.x / CR::NQ, n = 4 * cg;
+  const int h = hq / (HQ / H);
+  typename R::T qv[CR::RPG], kv[CR::RPG];
+  f32x4 dkv[CR::RPG];
+#pragma unroll
+  for (int i = 0; i < CR::RPG; ++i) {
+    const int r = min(r0 + grp * CR::RPG + i, L - 1);
+    const int64_t t = bos + r;
+    qv[i] = R::ld(q + (t * HQ + hq) * DK + n);
+    dqv[i] = ld4f(dq32 + (t * HQ + hq) * DK + n);
+    kv[i] = R::ld(k + (t * H + h) * DK + n);
+    dkv[i] = ld4f(dk_part + (t * HQ + hq) * DK + n);
+  }
+#pragma unroll
+  for (int i = 0; i < CR::RPG; ++i) {
+    const bool ok = r0 + grp * CR::RPG + i < L;
+    x[i] = ok ? R::cvt(qv[i]) * dqv[i] - R::cvt(kv[i]) * dkv[i] : f32x4{};
+  }
+}
+
 // Per (chunk, head, segment): totals of dP (per channel) and dGs over the
 // chunk, dP_tn = q_tn dq_tn - k_tn dk(hq)_tn, dGs_t = rows_ds - cols_ds.
-// grid (NCmax*HQ, nseg), 256 threads.
+// grid (NCmax*HQ, nseg), 256 threads; the row groups' sums meet in LDS.
 template <typename TE, int DK>
 __global__ __launch_bounds__(256) void k_bwd_chunk_totals(
     const TE *__restrict__ q, const TE *__restrict__ k, const float *__restrict__ dq32,
     const float *__restrict__ dk_part, const float *__restrict__ rows_ds,
     const float *__restrict__ cols_ds, float *__restrict__ ctot, const int32_t *__restrict__ cu,
     int64_t T, int HQ, int H, int NCmax) {
+  typedef ChunkRows<DK> CR;
   const int c = blockIdx.x % NCmax, hq = blockIdx.x / NCmax, s = blockIdx.y;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
   const int L = (int)min(eos - bos, (int64_t)NCmax * XC);
   const int r0 = c * XC;
-  float *out = ctot + (((int64_t)s * NCmax + c) * HQ + hq) * (DK + 1);
-  const int h = hq / (HQ / H);
-  for (int n = threadIdx.x; n <= DK; n += 256) {
-    float acc = 0.f;
-    for (int r = r0; r < min(r0 + XC, L); ++r) {
-      const int64_t t = bos + r;
-      if (n < DK)
-        acc += Elem<TE>::ld(q + (t * HQ + hq) * DK + n) * dq32[(t * HQ + hq) * DK + n] -
-               Elem<TE>::ld(k + (t * H + h) * DK + n) * dk_part[(t * HQ + hq) * DK + n];
-      else
-        acc += rows_ds[t * HQ + hq] - cols_ds[t * HQ + hq];
-    }
-    out[n] = acc;
+  float *out = ctot + (((int64_t)s * NCmax + c) * HQ + hq) * ctot_stride<DK>();
+  const int cg = threadIdx.x % CR::NQ, grp = threadIdx.x / CR::NQ;
+  if (r0 >= L) {  // a chunk slot past the sequence: zero totals (never read)
+    if (threadIdx.x <= DK) out[threadIdx.x] = 0.f;
+    return;
+  }
+  f32x4 x[CR::RPG], dqv[CR::RPG];
+  chunk_dp<TE, DK>(q, k, dq32, dk_part, bos, r0, L, HQ, H, hq, x, dqv);
+  f32x4 acc = x[0];
+#pragma unroll
+  for (int i = 1; i < CR::RPG; ++i) acc += x[i];
+  __shared__ f32x4 red[CR::NG][CR::NQ];
+  red[grp][cg] = acc;
+  // dGs over the chunk's rows: the second wave, one row per lane
+  if (threadIdx.x >= 64 && threadIdx.x < 128) {
+    const int r = r0 + (int)threadIdx.x - 64;
+    float y = r < L ? rows_ds[(bos + r) * HQ + hq] - cols_ds[(bos + r) * HQ + hq] : 0.f;
+    y = wave_sum(y);
+    if (threadIdx.x == 64) out[DK] = y;
+  }
+  __syncthreads();
+  if (grp == 0) {
+#pragma unroll
+    for (int q2 = 1; q2 < CR::NG; ++q2) acc += red[q2][cg];
+    *reinterpret_cast<f32x4 *>(out + 4 * cg) = acc;
   }
 }
 
 // Reverse running sums: dg (and dg_scalar) of chunk c = the totals of the
 // later chunks plus the in-chunk reverse inclusive sums; dq in the output
-// type.  grid (NCmax*HQ, nseg), 256 threads.
+// type.  grid (NCmax*HQ, nseg), 256 threads: each thread scans its own rows,
+// the row groups' totals and the later chunks' totals meet in LDS.
 template <typename TE, int DK>
 __global__ __launch_bounds__(256) void k_bwd_scan(
     const TE *__restrict__ q, const TE *__restrict__ k, const float *__restrict__ dq32,
@@ -342,6 +426,8 @@ __global__ __launch_bounds__(256) void k_bwd_scan(
     const float *__restrict__ cols_ds, const float *__restrict__ ctot, TE *__restrict__ dq,
     TE *__restrict__ dg, TE *__restrict__ dgs, const int32_t *__restrict__ cu, int64_t T, int HQ,
     int H, int NCmax) {
+  typedef ChunkRows<DK> CR;
+  constexpr int CS = ctot_stride<DK>();
   const int c = blockIdx.x % NCmax, hq = blockIdx.x / NCmax, s = blockIdx.y;
   int64_t bos, eos;
   segment_bounds(s, T, cu, bos, eos);
@@ -349,23 +435,47 @@ __global__ __launch_bounds__(256) void k_bwd_scan(
   const int nch = (L + XC - 1) / XC;
   if (c >= nch) return;
   const int r0 = c * XC;
-  const int h = hq / (HQ / H);
-  for (int n = threadIdx.x; n <= DK; n += 256) {
-    if (n == DK && dgs == nullptr) continue;
-    float acc = 0.f;
-    for (int c2 = c + 1; c2 < nch; ++c2) acc += ctot[(((int64_t)s * NCmax + c2) * HQ + hq) * (DK + 1) + n];
-    for (int r = min(r0 + XC, L) - 1; r >= r0; --r) {
+  const int cg = threadIdx.x % CR::NQ, grp = threadIdx.x / CR::NQ, n = 4 * cg;
+  const float *tots = ctot + ((int64_t)s * NCmax * HQ + hq) * CS;  // chunk c2's row: + c2 * HQ * CS
+  // totals of the later chunks, split over the row groups
+  f32x4 later = f32x4{};
+  for (int c2 = c + 1 + grp; c2 < nch; c2 += CR::NG) later += ld4f(tots + (int64_t)c2 * HQ * CS + n);
+  f32x4 x[CR::RPG], dqv[CR::RPG];
+  chunk_dp<TE, DK>(q, k, dq32, dk_part, bos, r0, L, HQ, H, hq, x, dqv);
+#pragma unroll
+  for (int i = CR::RPG - 2; i >= 0; --i) x[i] += x[i + 1];  // reverse inclusive, within the thread's rows
+  __shared__ f32x4 red[CR::NG][CR::NQ], lat[CR::NG][CR::NQ];
+  red[grp][cg] = x[0];
+  lat[grp][cg] = later;
+  // dg_scalar: the first wave, one row per lane
+  if (dgs != nullptr && threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int r = r0 + lane;
+    float y = r < L ? rows_ds[(bos + r) * HQ + hq] - cols_ds[(bos + r) * HQ + hq] : 0.f;
+    float lt = 0.f;
+    for (int c2 = c + 1 + lane; c2 < nch; c2 += 64) lt += tots[(int64_t)c2 * HQ * CS + DK];
+    lt = wave_sum(lt);
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {  // reverse inclusive scan over the lanes
+      const float v = __shfl_down(y, d);
+      if (lane + d < 64) y += v;
+    }
+    if (r < L) Elem<TE>::st(dgs + (bos + r) * HQ + hq, y + lt);
+  }
+  __syncthreads();
+  f32x4 add = f32x4{};
+#pragma unroll
+  for (int q2 = 0; q2 < CR::NG; ++q2) {
+    add += lat[q2][cg];
+    if (q2 > grp) add += red[q2][cg];
+  }
+#pragma unroll
+  for (int i = 0; i < CR::RPG; ++i) {
+    const int r = r0 + grp * CR::RPG + i;
+    if (r < L) {
       const int64_t t = bos + r;
-      if (n < DK) {
-        const float dqv = dq32[(t * HQ + hq) * DK + n];
-        acc += Elem<TE>::ld(q + (t * HQ + hq) * DK + n) * dqv -
-               Elem<TE>::ld(k + (t * H + h) * DK + n) * dk_part[(t * HQ + hq) * DK + n];
-        Elem<TE>::st(dg + (t * HQ + hq) * DK + n, acc);
-        Elem<TE>::st(dq + (t * HQ + hq) * DK + n, dqv);
-      } else {
-        acc += rows_ds[t * HQ + hq] - cols_ds[t * HQ + hq];
-        Elem<TE>::st(dgs + t * HQ + hq, acc);
-      }
+      st4<TE>(dg + (t * HQ + hq) * DK + n, x[i] + add);
+      st4<TE>(dq + (t * HQ + hq) * DK + n, dqv[i]);
     }
   }
 }
@@ -508,7 +618,7 @@ size_t bwd_workspace_layout(const FwdProblem &p, BwdWorkspace *bw, char *base) {
   float *dv_part = take(sizeof(float) * nrows * p.V);
   float *rows_ds = take(sizeof(float) * nrows);
   float *cols_ds = take(sizeof(float) * nrows);
-  float *ctot = take(sizeof(float) * p.nseg * NCmax * p.HQ * (p.K + 1));
+  float *ctot = take(sizeof(float) * p.nseg * NCmax * p.HQ * (p.K + 4));
   float *dsp = take(sizeof(float) * ((p.ntok + DS_TOK - 1) / DS_TOK) * p.HQ);
   float *qbh = take(p.dtype == WA_DT_BF16 ? sizeof(uint16_t) * nrows * p.K : 0);
   if (bw) {

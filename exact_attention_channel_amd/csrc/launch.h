@@ -62,7 +62,7 @@ struct BwdWorkspace {
   float *Dv, *psD;                  // [ntok, HQ] D_i, exp(sink - lse_i) D_i
   float *dq32, *dk_part, *dv_part;  // [ntok, HQ, K|V]: dq, each query head's dk and dv
   float *rows_ds, *cols_ds;         // [ntok, HQ] row and column sums of ds
-  float *ctot;                      // [nseg*NCmax, HQ, K+1] chunk totals of dP and dGs
+  float *ctot;                      // [nseg*NCmax, HQ, K+4] chunk totals of dP (K) and dGs (at K), padded
   float *dsp;                       // [ceil(ntok/1024), HQ] partial sums of dsink
   void *qbh;                        // bf16 inputs: [HQ, ntok, K] half q_hat for the MFMA kernels
 };
