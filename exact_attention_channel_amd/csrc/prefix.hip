@@ -54,6 +54,25 @@ template <> __device__ __forceinline__ FV<8> loadv<float, 8>(const float *p) {
   const float4 x = reinterpret_cast<const float4 *>(p)[0], y = reinterpret_cast<const float4 *>(p)[1];
   return FV<8>{{x.x, x.y, x.z, x.w, y.x, y.y, y.z, y.w}};
 }
+// A row past the chunk's last one: its channels read as zero.  Loads of
+// such rows fetch the chunk's last row instead (every load unconditional),
+// so that the compiler issues a thread's loads together instead of waiting
+// for each one inside its own branch.
+template <int N> __device__ __forceinline__ FV<N> keep_if(bool ok, FV<N> x) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) x.v[j] = ok ? x.v[j] : 0.f;
+  return x;
+}
+// One element kept as raw bits (loaded early, converted where used).
+template <typename TE> struct RawElem;
+template <> struct RawElem<bf16_t> {
+  static __device__ __forceinline__ uint32_t ld(const bf16_t *p) { return *p; }
+  static __device__ __forceinline__ float cvt(uint32_t b) { return __uint_as_float(b << 16); }
+};
+template <> struct RawElem<float> {
+  static __device__ __forceinline__ uint32_t ld(const float *p) { return __float_as_uint(*p); }
+  static __device__ __forceinline__ float cvt(uint32_t b) { return __uint_as_float(b); }
+};
 // The same 16 bytes kept raw (loaded early, converted where used).
 __device__ __forceinline__ u32x4 load16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 template <typename TE, int N> __device__ __forceinline__ FV<N> fromraw(u32x4 w);
@@ -160,14 +179,20 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
   FV<CPT> xs[CHUNK / NG];
 #pragma unroll
   for (int i = 0; i < CHUNK / NG; ++i) {
-    const int r = grp + i * NG;
-    xs[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
+    const int r = min(grp + i * NG, nrow - 1);
+    xs[i] = loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi);
   }
+  // this row's g_scalar (first wave), loaded with the rest (raw bits; a valid
+  // dummy address without a gate)
+  const uint32_t gs_bits =
+      RawElem<TE>::ld(gs != nullptr ? gs + (r0 + min((int)(threadIdx.x & 63), nrow - 1)) * HQ + hq : g);
   FV<CPT> acc = zerov<CPT>();
 #pragma unroll
-  for (int i = 0; i < CHUNK / NG; ++i)
+  for (int i = 0; i < CHUNK / NG; ++i) {
+    const FV<CPT> x = keep_if<CPT>(grp + i * NG < nrow, xs[i]);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) acc.v[j] += xs[i].v[j];
+    for (int j = 0; j < CPT; ++j) acc.v[j] += x.v[j];
+  }
   __shared__ FV<CPT> red[NG][NQ];
   red[grp][cgi] = acc;
   __syncthreads();
@@ -180,7 +205,7 @@ __global__ __launch_bounds__(256) void k_chunk_sums(const TE *__restrict__ g,
     storev<float, CPT>(csum + (cidx * HQ + hq) * KD + CPT * cgi, acc);
   }
   if (gs != nullptr && threadIdx.x < 64) {
-    float a = (int)threadIdx.x < nrow ? Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.f;
+    float a = (int)threadIdx.x < nrow ? RawElem<TE>::cvt(gs_bits) : 0.f;
     a = wave_sum(a);
     if (threadIdx.x == 0) csum_s[cidx * HQ + hq] = a;
   }
@@ -289,8 +314,12 @@ struct ChunkScan {
     __shared__ FV<CPT> tot[NG][NQ];
 #pragma unroll
     for (int i = 0; i < RPG; ++i) {
-      const int r = grp * RPG + i;
-      p2[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
+      const int r = min(grp * RPG + i, nrow - 1);
+      p2[i] = loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi);
+    }
+#pragma unroll
+    for (int i = 0; i < RPG; ++i) {
+      p2[i] = keep_if<CPT>(grp * RPG + i < nrow, p2[i]);
       if (i > 0)
 #pragma unroll
         for (int j = 0; j < CPT; ++j) p2[i].v[j] += p2[i - 1].v[j];
@@ -351,12 +380,6 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   // anchor of the query tile (its first chunk): q_hat = q 2^(P2 - RQ)
   const int64_t cq = (int64_t)s * NCmax + (c & ~1);
   const FV<CPT> RQ = loadv<float, CPT>(anch + (cq * HQ + hq) * KD + CPT * cgi);
-  // the gate's chunk offset and this row's g_scalar (first wave)
-  float gs_x = 0.f, gs_off = 0.f;
-  if (gs != nullptr && threadIdx.x < 64) {
-    gs_x = (int)threadIdx.x < nrow ? Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.f;
-    gs_off = off_s[cidx * HQ + hq];
-  }
   // the rows' keys (and queries, where this pass rescales them) load
   // together with g, ahead of the in-chunk scan: every load of the
   // workgroup goes out in one memory round trip
@@ -364,12 +387,18 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   u32x4 kin[CS::RPG], qin[CS::RPG];
 #pragma unroll
   for (int i = 0; i < CS::RPG; ++i) {
-    const int r = grp * CS::RPG + i;
-    const int64_t t = r0 + r;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    kin[i] = r < nrow ? load16(k + (t * H + h) * KD + CPT * cgi) : z;
-    qin[i] = QL && r < nrow ? load16(q + (t * HQ + hq) * KD + CPT * cgi) : z;
+    // rows past the chunk load its last row (unconditional loads; never stored)
+    const int64_t t = r0 + min(grp * CS::RPG + i, nrow - 1);
+    kin[i] = load16(k + (t * H + h) * KD + CPT * cgi);
+    if (QL) qin[i] = load16(q + (t * HQ + hq) * KD + CPT * cgi);
   }
+  // the gate's chunk offset and this row's g_scalar (used by the first
+  // wave), kept as raw bits until used; every thread loads (the same 64 rows
+  // per wave), and without a gate a valid dummy address is read, so that no
+  // branch holds a wait
+  const TE *gsp = gs != nullptr ? gs + (r0 + min((int)(threadIdx.x & 63), nrow - 1)) * HQ + hq : g;
+  const uint32_t gs_bits = RawElem<TE>::ld(gsp);
+  const float gs_off = gs != nullptr ? off_s[cidx * HQ + hq] : 0.f;
   FV<CPT> p2[CS::RPG];
   CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
   // Range of the anchored operands: the exponents of q_hat and k_tilde stay
@@ -424,7 +453,7 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
     const int r = threadIdx.x;
     float G = 0.f;
     if (gs != nullptr) {
-      const float x = wave_inclusive_scan(gs_x);
+      const float x = wave_inclusive_scan(r < nrow ? RawElem<TE>::cvt(gs_bits) : 0.f);
       G = (gs_off + x) * LOG2E;
       if (r < nrow) gsum[(r0 + r) * HQ + hq] = G;
       // the half keys carry -G split into two halves
