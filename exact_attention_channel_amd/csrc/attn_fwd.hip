@@ -579,9 +579,11 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
   // block) and, with RB, rebuilds each k-step of the query operand for the
   // tile after next right after the score MFMA that last reads it, from the
   // factors last published (the first block of a steady pair, whose tile
-  // after next starts a chunk).
+  // after next starts a chunk).  A tile that crosses the window edge of the
+  // wave's rows (mk: its first key, else -1) is masked before its
+  // exponentials.
   auto fused = [&](auto rb_c, f32x16 &Sc, f32x16 &Sn, const unsigned char *Vb, const unsigned char *Kb,
-                   int Jk, unsigned char *kbuf, int Jv, unsigned char *vbuf, bool kdo) {
+                   int Jk, unsigned char *kbuf, int Jv, unsigned char *vbuf, bool kdo, int mk) {
     constexpr bool RB = decltype(rb_c)::value;
     constexpr int NP = 2 * NMB;
     constexpr FusedOrder<NKS, NP, 4> FO{};
@@ -601,6 +603,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     };
     if (KR >= 0 && kdo && wv + NWV * KR < BT::NKI) dma16(kt_rs, kbuf + 1024 * (wv + NWV * KR), koff[KR], Jk * BK * KRB);
     if (VR >= 0 && wv + NWV * VR < BT::NVI) dma16(v_rs, vbuf + 1024 * (wv + NWV * VR), voff[VR], Jv * BK * vrow * 2);
+    if (mk >= 0) mask(Sc, mk);
     float pr[16];
     bf16x8 pb[2];
     float rs = 0.f;
@@ -776,29 +779,32 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       vm_wait0();
     };
     // A pair of tiles t (even, the first of an anchor chunk) and t + 1, both
-    // older than the query tile's own key tiles, outside the window edge,
-    // with every row's reference set and sigma = 0 for their chunk, with
-    // tiles up to t + 4 still to come: body() would take its steady-state
-    // block for both, rebuild inside the first one and publish the factors
-    // of chunk(t + 4) after the second one.  The same work with every
-    // condition known in advance.
+    // older than the query tile's own key tiles, with every row's reference
+    // set and sigma = 0 for their chunk, with tiles up to t + 4 still to
+    // come: body() would take its steady-state block for both, rebuild
+    // inside the first one and publish the factors of chunk(t + 4) after the
+    // second one.  The same work with every condition known in advance.  A
+    // tile at the window edge is masked inside the block; a tile that lies
+    // wholly below the wave's window then adds nothing (body() would skip
+    // it for this wave).
     auto pair_ok = [&](int t) -> bool {
       if (MODE == 1 || t < ND || t + 2 >= NTL) return false;
-      const int J = tileJ(t);
-      if ((J & 1) || (window > 0 && qw0 + 31 - J * BK >= window)) return false;
+      if (tileJ(t) & 1) return false;
       return __ballot(!(all_set && cs_cur == 1.f && cs_next == 1.f)) == 0;
     };
+    // first key of tile J when it crosses the window edge of the wave's rows
+    auto edge = [&](int J) { return window > 0 && qw0 + 31 - J * BK >= window ? J * BK : -1; };
     auto steady_pair = [&](int t) {
       const int J = tileJ(t);  // tiles t .. t + 3 are J .. J + 3
       __syncthreads();
-      fused(std::true_type{}, Sa, Sb, V0, K1, J + 2, K0, J + 1, V1, true);
+      fused(std::true_type{}, Sa, Sb, V0, K1, J + 2, K0, J + 1, V1, true, edge(J));
       cs_cur = cs_next;
       cs_next = cs_next2;
       vm_wait0();
       __syncthreads();
       const bool nc4 = t + 4 < NTL;  // tile t + 4 exists (and starts a chunk)
       if (nc4) load_a((J + 4) >> 1);
-      fused(std::false_type{}, Sb, Sa, V1, K0, J + 3, K1, J + 2, V0, t + 3 < NTL);
+      fused(std::false_type{}, Sb, Sa, V1, K0, J + 3, K1, J + 2, V0, t + 3 < NTL, edge(J + 1));
       float cs3 = cs_next2;
       if (nc4) cs3 = factors();
       cs_cur = cs_next;

@@ -64,6 +64,13 @@ def run_oracle(x, rows=None):
                             cu_seqlens=x["cu_seqlens"], rows=rows, return_lse=True)
 
 
+def assert_repeatable(wa, x, o, lse, what):
+    """A second launch on the same inputs returns the same bits (no atomics,
+    fixed reduction orders)."""
+    o2, lse2 = run_gpu(wa, x)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2), what + ": second launch differs"
+
+
 def check(got, ref, tol, what):
     err = np.abs(got - ref)
     i = np.unravel_index(np.argmax(err), err.shape)
@@ -211,6 +218,7 @@ def test_prefill_gate_favouring_old_keys(wa, c):
     ro, rl = run_oracle(x)
     check(o, ro, TOL[c.dtype], c.name + " o")
     check(lse, rl, lse_tol(c.dtype, rl), c.name + " lse")
+    assert_repeatable(wa, x, o, lse, c.name)  # the recompute path, run twice
 
 
 WIDE = [
@@ -245,6 +253,7 @@ def test_prefill_out_of_operand_range(wa, c):
     ro, rl = run_oracle(x)
     check(o, ro, TOL[c.dtype], c.name + " o")
     check(lse, rl, lse_tol(c.dtype, rl), c.name + " lse")
+    assert_repeatable(wa, x, o, lse, c.name)  # the exact path, run twice
 
 
 def boundary_rows(bos, eos, step=64, extra=()):
@@ -293,6 +302,7 @@ def test_config_varlen_window_rows(wa):
     N = o.shape[1]
     check(o.reshape(N, c.HQ, c.V)[rows], ro, 2e-2, c.name + f" ({len(rows)} rows)")
     check(lse.reshape(N, c.HQ)[rows], rl, lse_tol(c.dtype, rl), c.name + " lse")
+    assert_repeatable(wa, x, o, lse, c.name)
 
 
 # ----------------------------------------------------------------------------- indexing probes
