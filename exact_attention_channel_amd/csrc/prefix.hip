@@ -495,16 +495,20 @@ __global__ __launch_bounds__(256) void k_chunk_sums_f64(const TE *__restrict__ g
   FV<CPT> xs[CHUNK / NG];
 #pragma unroll
   for (int i = 0; i < CHUNK / NG; ++i) {
-    const int r = grp + i * NG;
-    xs[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
+    const int r = min(grp + i * NG, nrow - 1);
+    xs[i] = loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi);
   }
+  const uint32_t gs_bits =
+      RawElem<TE>::ld(gs != nullptr ? gs + (r0 + min((int)(threadIdx.x & 63), nrow - 1)) * HQ + hq : g);
   double acc[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) acc[j] = 0.0;
 #pragma unroll
-  for (int i = 0; i < CHUNK / NG; ++i)
+  for (int i = 0; i < CHUNK / NG; ++i) {
+    const FV<CPT> x = keep_if<CPT>(grp + i * NG < nrow, xs[i]);
 #pragma unroll
-    for (int j = 0; j < CPT; ++j) acc[j] += (double)xs[i].v[j];
+    for (int j = 0; j < CPT; ++j) acc[j] += (double)x.v[j];
+  }
   __shared__ double red[NG][KD];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) red[grp][CPT * cgi + j] = acc[j];
@@ -516,7 +520,7 @@ __global__ __launch_bounds__(256) void k_chunk_sums_f64(const TE *__restrict__ g
     csum[(cidx * HQ + hq) * KD + ch] = t;
   }
   if (gs != nullptr && threadIdx.x < 64) {
-    double a = (int)threadIdx.x < nrow ? (double)Elem<TE>::ld(gs + (r0 + threadIdx.x) * HQ + hq) : 0.0;
+    double a = (int)threadIdx.x < nrow ? (double)RawElem<TE>::cvt(gs_bits) : 0.0;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) a += __shfl_xor(a, o);
     if (threadIdx.x == 0) csum_s[cidx * HQ + hq] = a;
@@ -612,23 +616,28 @@ __global__ __launch_bounds__(256) void k_prefix_write_f64(const TE *__restrict__
   FV<CPT> xs[RPG];
 #pragma unroll
   for (int i = 0; i < RPG; ++i) {
-    const int r = grp * RPG + i;
-    xs[i] = r < nrow ? loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi) : zerov<CPT>();
+    const int r = min(grp * RPG + i, nrow - 1);
+    xs[i] = loadv<TE, CPT>(g + ((r0 + r) * HQ + hq) * KD + CPT * cgi);
   }
+  // the chunk offsets and this row's g_scalar load with the rows
+  double base[CPT];
+#pragma unroll
+  for (int j = 0; j < CPT; ++j) base[j] = off[(cidx * HQ + hq) * KD + CPT * cgi + j];
+  const uint32_t gs_bits =
+      RawElem<TE>::ld(gs != nullptr ? gs + (r0 + min((int)(threadIdx.x & 63), nrow - 1)) * HQ + hq : g);
   double acc[CPT];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) acc[j] = 0.0;
 #pragma unroll
-  for (int i = 0; i < RPG; ++i)
+  for (int i = 0; i < RPG; ++i) {
+    xs[i] = keep_if<CPT>(grp * RPG + i < nrow, xs[i]);
 #pragma unroll
     for (int j = 0; j < CPT; ++j) acc[j] += (double)xs[i].v[j];
+  }
   __shared__ double tot[NG][KD];
 #pragma unroll
   for (int j = 0; j < CPT; ++j) tot[grp][CPT * cgi + j] = acc[j];
   __syncthreads();
-  double base[CPT];
-#pragma unroll
-  for (int j = 0; j < CPT; ++j) base[j] = off[(cidx * HQ + hq) * KD + CPT * cgi + j];
   for (int q = 0; q < grp; ++q)
 #pragma unroll
     for (int j = 0; j < CPT; ++j) base[j] += tot[q][CPT * cgi + j];
@@ -645,7 +654,7 @@ __global__ __launch_bounds__(256) void k_prefix_write_f64(const TE *__restrict__
   }
   if (gs != nullptr && threadIdx.x < 64) {
     const int r = threadIdx.x;
-    double x = r < nrow ? (double)Elem<TE>::ld(gs + (r0 + r) * HQ + hq) : 0.0;
+    double x = r < nrow ? (double)RawElem<TE>::cvt(gs_bits) : 0.0;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const double y = __shfl_up(x, d);
