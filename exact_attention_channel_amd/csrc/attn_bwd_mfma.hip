@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_w16(
   constexpr int NCK = DK / 16, NCV = DV / 16;        // 16-channel blocks of dK^T and dV^T
   constexpr int SA = 3 * XC;                         // statistics: L, D, G of the rows
   constexpr int NCP = QB / (XC * 4) < 64 ? QB / (XC * 4) : 64;  // channels per epilogue pass
+  constexpr int RA = 4;                              // products an LDS operand is read ahead
   static_assert(NQD % 4 == 0 && NOD % 4 == 0, "a block is a multiple of 4 KiB");
   __shared__ __attribute__((aligned(16))) unsigned char Qb0[QB], Qb1[QB];
   __shared__ __attribute__((aligned(16))) unsigned char Ob0[OB], Ob1[OB];
@@ -305,22 +306,35 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_w16(
     }
     const _Float16 *Qh = reinterpret_cast<const _Float16 *>(Qb);
     const bf16_t *Oh = reinterpret_cast<const bf16_t *>(Ob);
-    // S = Q'' k_tilde^T and dP = dO v^T: four 16-row tiles
+    // S = Q'' k_tilde^T and dP = dO v^T: four 16-row tiles, one sequence of
+    // products whose LDS operands are read RA products ahead (sched_barrier
+    // keeps each step's read and product together, so the compiler does not
+    // pull every read down to the product that uses it)
     f32x4 S[4], dPt[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) S[t] = dPt[t] = f32x4{};
+    {
+      constexpr int NS1 = 4 * NSK, NS2 = NS1 + 4 * NSV;
+      u32x4 op[NS2];
+      auto rd = [&](int i) {
+        if (i < NS1)
+          op[i] = *reinterpret_cast<const u32x4 *>(Qh + qpiece<DK>(16 * (i % 4) + c16, 4 * (i / 4) + gq));
+        else
+          op[i] = *reinterpret_cast<const u32x4 *>(Oh + qpiece<DV>(16 * (i % 4) + c16, 4 * ((i - NS1) / 4) + gq));
+      };
 #pragma unroll
-    for (int s = 0; s < NSK; ++s)
+      for (int i = 0; i < RA; ++i) rd(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        S[t] = Mfma16<_Float16>::run(
-            *reinterpret_cast<const f16x8 *>(Qh + qpiece<DK>(16 * t + c16, 4 * s + gq)), kr[s], S[t]);
-#pragma unroll
-    for (int s = 0; s < NSV; ++s)
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        dPt[t] = Mfma16<bf16_t>::run(
-            *reinterpret_cast<const bf16x8 *>(Oh + qpiece<DV>(16 * t + c16, 4 * s + gq)), vr[s], dPt[t]);
+      for (int i = 0; i < NS2; ++i) {
+        if (i + RA < NS2) rd(i + RA);
+        if (i < NS1)
+          S[i % 4] = Mfma16<_Float16>::run(__builtin_bit_cast(f16x8, op[i]), kr[i / 4], S[i % 4]);
+        else
+          dPt[i % 4] = Mfma16<bf16_t>::run(__builtin_bit_cast(bf16x8, op[i]), vr[(i - NS1) / 4], dPt[i % 4]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     // probabilities and ds: lane's key kw, rows 16 t + 4 (lane/16) + e
     const int i0 = I * XC, nq = min(XC, L - i0);
     const bool full = nq == XC && nk == XC && I > J && !(window > 0 && i0 + XC - 1 - j0 >= window);
@@ -349,17 +363,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkdv_w16(
         csum += ds;
       }
     }
-    // dV^T += dO^T P, dK^T += Q''^T ds over two 32-row steps
+    // dV^T += dO^T P, dK^T += Q''^T ds over two 32-row steps, the
+    // transposed operands read RA products ahead as above
+    {
+      const bf16x8 pb[2] = {pack_b(pv), pack_b(pv + 8)};
+      const f16x8 db[2] = {pack_h(dsv), pack_h(dsv + 8)};
+      constexpr int NT = NCV + NCK, NT2 = 2 * NT;
+      u32x4 op[NT2];
+      auto rd = [&](int i) {
+        const int u = i / NT, k = i % NT;
+        if (k < NCV)
+          op[i] = __builtin_bit_cast(u32x4, tr16_operand<bf16_t, DV>(Oh, 32 * u, 16 * k, lane));
+        else
+          op[i] = __builtin_bit_cast(u32x4, tr16_operand<_Float16, DK>(Qh, 32 * u, 16 * (k - NCV), lane));
+      };
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const bf16x8 pb = pack_b(pv + 8 * u);
-      const f16x8 db = pack_h(dsv + 8 * u);
+      for (int i = 0; i < RA; ++i) rd(i);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int cb = 0; cb < NCV; ++cb)
-        dVa[cb] = Mfma16<bf16_t>::run(tr16_operand<bf16_t, DV>(Oh, 32 * u, 16 * cb, lane), pb, dVa[cb]);
-#pragma unroll
-      for (int cb = 0; cb < NCK; ++cb)
-        dKa[cb] = Mfma16<_Float16>::run(tr16_operand<_Float16, DK>(Qh, 32 * u, 16 * cb, lane), db, dKa[cb]);
+      for (int i = 0; i < NT2; ++i) {
+        if (i + RA < NT2) rd(i + RA);
+        const int u = i / NT, k = i % NT;
+        if (k < NCV)
+          dVa[k] = Mfma16<bf16_t>::run(__builtin_bit_cast(bf16x8, op[i]), pb[u], dVa[k]);
+        else
+          dKa[k - NCV] = Mfma16<_Float16>::run(__builtin_bit_cast(f16x8, op[i]), db[u], dKa[k - NCV]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     return true;
   };
