@@ -169,7 +169,7 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     const float *__restrict__ anch, const float *__restrict__ gsum,
     const float *__restrict__ sink, bf16_t *__restrict__ o, float *__restrict__ lse,
     const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ, int H, int nseg, int NCmax,
-    int NQT, int window, float qscale, const int *__restrict__ wide) {
+    int NQT, int window, float qscale, const int *__restrict__ wide, const float *__restrict__ mid) {
   // Score product per 32-key tile and wave: S^T = K_tilde Q'^T over DK + 16
   // channels.  The key rows come from the pre-pass with their extra block
   // [1, 1, -Gs_j hi, -Gs_j lo, 0 ...]; the wave's query operand Q' holds
@@ -291,10 +291,14 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     // acc: the exponent of q_hat's factor in log2 units, with log2(qscale)
     // folded in, so that each row costs one fma, one exp2 and one multiply
     // per channel: acc = P2 - RQ_I + log2(qscale), P2 = (offset + g sum) log2(e)
+    // A wave of the chunk's second 32 rows starts from the pre-pass's
+    // running sum at row 31 (log2 units), the others from the chunk offset.
     const float lq = __builtin_amdgcn_logf(qscale);
+    const float *a0 = (second ? mid : off) + ((cbase + cw) * HQ + hq) * DK + CPL * lane;
+    const float a_scale = second ? 1.f : LOG2E;
     float acc[CPL];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = off[((cbase + cw) * HQ + hq) * DK + CPL * lane + c] * LOG2E - rq[c] + lq;
+    for (int c = 0; c < CPL; ++c) acc[c] = a0[c] * a_scale - rq[c] + lq;
     // buffer loads: the row offset is a scalar, and rows past the sequence
     // read as zero without a branch per row
     const int64_t ext = ((int64_t)(L - 1) * qrow + DK) * 2;
@@ -305,17 +309,11 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
       if (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(*rs, 4 * lane, r * qrow * 2, 0);
       return __builtin_amdgcn_raw_buffer_load_b16(*rs, 2 * lane, r * qrow * 2, 0);
     };
-    uint32_t gp[32], gw[32], qw[32];  // g of the chunk's first half (second-half waves), g and q of the rows
+    uint32_t gw[32], qw[32];  // g and q of the rows
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
-      gp[u] = second ? ld(g_b, r0 + u) : 0u;
       gw[u] = ld(g_b, qw0 + u);
       qw[u] = ld(q_b, qw0 + u);
-    }
-#pragma unroll
-    for (int u = 0; u < 32; ++u) {
-      acc[0] = fmaf(bf16_lo(gp[u]), LOG2E, acc[0]);
-      if (CPL == 2) acc[CPL - 1] = fmaf(bf16_hi(gp[u]), LOG2E, acc[CPL - 1]);
     }
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
@@ -1006,7 +1004,7 @@ hipError_t attn_bf16_t(const FwdProblem &p, const FwdWorkspace &ws, hipStream_t 
                        ws.anch, ws.gsum, p.sink, static_cast<bf16_t *>(p.o), p.lse, p.cu, p.T,
                        p.ntok, (int)p.HQ, (int)p.H, (int)p.nseg, NCmax, NQT,
                        (int)(p.window > 0 && p.window < p.maxlen ? p.window : 0), p.scale * LOG2E,
-                       ws.wide);
+                       ws.wide, ws.mid);
   };
   if (p.g_scalar != nullptr)
     args(k_attn_fwd_bf16<DK, DV, true>);

@@ -36,6 +36,8 @@ struct FwdWorkspace {
   float *gsum;     // [ntok, HQ] running gate sum (log2 units)
   int *wide;       // [nseg, HQ] 1: the (segment, head) leaves the anchored operands' range
   void *qbh;       // NULL, or the backward's half q_hat [HQ, ntok, K] (own-chunk anchor)
+  float *mid;      // bf16 path: [nseg*NCmax, HQ, K] running sum of g (log2 units) at each
+                   // chunk's row 31, where the second 32-row half of a query tile's chunk starts
 };
 
 size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base);

@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
     const float *__restrict__ off_s, TO *__restrict__ qh, TO *__restrict__ kt,
     float *__restrict__ gsum, const int32_t *__restrict__ cu, int64_t T, int64_t ntok, int HQ,
     int H, int NCmax, float qscale, ChunkGrid cg, int *__restrict__ wide,
-    _Float16 *__restrict__ qbh) {
+    _Float16 *__restrict__ qbh, float *__restrict__ mid) {
   constexpr bool HM = std::is_same<TO, _Float16>::value;  // head-major rows with extras
   constexpr int KX = HM ? KD + 16 : KD;
   int hq, c;
@@ -401,6 +401,10 @@ __global__ __launch_bounds__(256) void k_prefill_operands(
   const float gs_off = gs != nullptr ? off_s[cidx * HQ + hq] : 0.f;
   FV<CPT> p2[CS::RPG];
   CS::run(g, r0, nrow, HQ, hq, cgi, grp, base, p2);
+  // half operands: the running sum at row 31, from which the attention
+  // kernel's waves for the chunk's second 32 rows start their own sums
+  if (HM && grp == 31 / CS::RPG && nrow > 32)
+    storev<float, CPT>(mid + (cidx * HQ + hq) * KD + CPT * cgi, p2[31 % CS::RPG]);
   // Range of the anchored operands: the exponents of q_hat and k_tilde stay
   // within EMAX (and the half keys and gate sums below their limits), else
   // the (segment, head) goes to the exact path.  The benchmark workloads
@@ -784,7 +788,7 @@ hipError_t prefix_phases_t(const FwdProblem &p, const FwdWorkspace &ws, hipStrea
                        static_cast<const TE *>(p.k), static_cast<const TE *>(p.g), gs, ws.csum,
                        ws.anch, ws.csum_s, static_cast<TO *>(ws.qh), static_cast<TO *>(ws.kt),
                        ws.gsum, p.cu, p.T, p.ntok, (int)p.HQ, (int)p.H, NCmax, qscale, cgC,
-                       ws.wide, static_cast<_Float16 *>(ws.qbh));
+                       ws.wide, static_cast<_Float16 *>(ws.qbh), ws.mid);
   };
   // the backward's half q_hat (bf16 inputs only) comes from its own instance
   if constexpr (std::is_same<TE, bf16_t>::value) {
@@ -866,6 +870,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
   char *kt = take(esz * p.ntok * p.HQ * (p.dtype == 0 ? p.K + 16 : p.K));
   char *gsum = take(sizeof(float) * p.ntok * p.HQ);
   char *wide = take(sizeof(int) * p.nseg * p.HQ);
+  char *mid = take(p.dtype == 0 ? sizeof(float) * nchunk * p.HQ * p.K : 0);
   if (ws) {
     ws->csum = reinterpret_cast<float *>(csum);
     ws->anch = reinterpret_cast<float *>(anch);
@@ -875,6 +880,7 @@ size_t fwd_workspace_layout(const FwdProblem &p, FwdWorkspace *ws, char *base) {
     ws->gsum = reinterpret_cast<float *>(gsum);
     ws->wide = reinterpret_cast<int *>(wide);
     ws->qbh = nullptr;  // the backward sets it to its own buffer
+    ws->mid = reinterpret_cast<float *>(mid);
   }
   return off;
 }
