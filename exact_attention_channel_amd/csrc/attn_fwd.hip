@@ -294,16 +294,56 @@ __global__ __launch_bounds__(64 * QTILE / 32, 2) void k_attn_fwd_bf16(
     // A wave of the chunk's second 32 rows starts from the pre-pass's
     // running sum at row 31 (log2 units), the others from the chunk offset.
     const float lq = __builtin_amdgcn_logf(qscale);
-    const float *a0 = (second ? mid : off) + ((cbase + cw) * HQ + hq) * DK + CPL * lane;
     const float a_scale = second ? 1.f : LOG2E;
-    float acc[CPL];
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] = a0[c] * a_scale - rq[c] + lq;
     // buffer loads: the row offset is a scalar, and rows past the sequence
     // read as zero without a branch per row
     const int64_t ext = ((int64_t)(L - 1) * qrow + DK) * 2;
     const __amdgpu_buffer_rsrc_t g_rs = make_rsrc(g + uniform64((bos64 * HQ + hq) * DK), uniform64(ext));
     const __amdgpu_buffer_rsrc_t q_rs = make_rsrc(q + uniform64((bos64 * HQ + hq) * DK), uniform64(ext));
+    if constexpr (DK == 64) {
+      // 64 channels: a lane takes two channels (4-byte loads), the lower
+      // half-wave rows 0..15 of the wave and the upper half rows 16..31;
+      // the upper half starts from the lower half's sum over its rows
+      const int cl = lane & 31, hr = lane >> 5;
+      const float *a0 = (second ? mid : off) + ((cbase + cw) * HQ + hq) * DK + 2 * cl;
+      const float *rq2 = anch_b + (int64_t)(2 * I) * HQ * DK + 2 * cl;
+      float acc2[2] = {a0[0] * a_scale - rq2[0] + lq, a0[1] * a_scale - rq2[1] + lq};
+      uint32_t gw[16], qw[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int voff = 4 * cl + hr * 16 * qrow * 2, soff = (qw0 + u) * qrow * 2;
+        gw[u] = __builtin_amdgcn_raw_buffer_load_b32(g_rs, voff, soff, 0);
+        qw[u] = __builtin_amdgcn_raw_buffer_load_b32(q_rs, voff, soff, 0);
+      }
+      float hs[2] = {0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        hs[0] += bf16_lo(gw[u]);
+        hs[1] += bf16_hi(gw[u]);
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float other = __shfl_xor(hs[c], 32);
+        if (hr == 1) acc2[c] = fmaf(other, LOG2E, acc2[c]);
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        acc2[0] = fmaf(bf16_lo(gw[u]), LOG2E, acc2[0]);
+        acc2[1] = fmaf(bf16_hi(gw[u]), LOG2E, acc2[1]);
+        const float q0 = bf16_lo(qw[u]) * fast_exp2(acc2[0]), q1 = bf16_hi(qw[u]) * fast_exp2(acc2[1]);
+        qmx = fmaxf(qmx, fmaxf(fabsf(q0), fabsf(q1)));
+        *reinterpret_cast<uint32_t *>(&Qs[(wv * 32 + 16 * hr + u) * QSB + 4 * cl]) = pack_f16x2(q0, q1);
+      }
+      qmx = wave_max(qmx);
+      int ex = 0;
+      (void)frexpf(qmx, &ex);  // qmx < 2^ex
+      qexp = __builtin_amdgcn_readfirstlane(max(ex, -8));
+      return;
+    }
+    const float *a0 = (second ? mid : off) + ((cbase + cw) * HQ + hq) * DK + CPL * lane;
+    float acc[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] = a0[c] * a_scale - rq[c] + lq;
     const __amdgpu_buffer_rsrc_t *g_b = &g_rs, *q_b = &q_rs;
     auto ld = [&](const __amdgpu_buffer_rsrc_t *rs, int r) -> uint32_t {
       if (CPL == 2) return __builtin_amdgcn_raw_buffer_load_b32(*rs, 4 * lane, r * qrow * 2, 0);
